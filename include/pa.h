@@ -1,0 +1,198 @@
+/*
+ * pa.h - C ABI of libpa, paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow four public pages on paged attention:
+ *   [Pico-vLLM]  "Pico-vLLM" write-up (zingnex forum): §1 model layer (RoPE,
+ *                GQA, in-place rotate_half), §2 kernel layer (paged prefill
+ *                kernel, paged decode kernel, fused RoPE + KV-cache store,
+ *                Flash-Attention-style tiling), H200 comparison (Flash Decode).
+ *   [mini-llm]   "mini-llm-engine" post (liangqianxing): §3.1 Paged KV Cache
+ *                (16-token physical blocks, per-sequence logical->physical
+ *                block table), §3.3 Chunked Prefill, §3.4 Prefix Caching
+ *                (blocks shared by several sequences, ref_count > 1).
+ *   [nano-vllm]  "nano-vllm" commentary (ai-stack), FAQ Q2 (KV cache stored
+ *                in non-contiguous fixed-size blocks through a table).
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers to dense row-major data, except where
+ *     a comment says "host".  bf16 tensors hold IEEE bfloat16 bit patterns.
+ *   - The caller owns all memory.  The library allocates nothing, keeps no
+ *     state between calls (apart from caching the device's properties) and
+ *     never synchronises: work is enqueued on `stream` and the call returns.
+ *   - Arguments are checked on the host before anything is enqueued; a bad
+ *     argument returns an error status and leaves every buffer untouched.  No
+ *     C++ exception crosses this interface.
+ *   - Device-side preconditions are NOT checked (reading device memory would
+ *     need a synchronisation); violating one is undefined behaviour:
+ *       * every block-table entry a call reads is in [0, num_blocks);
+ *       * the non-negative slots of one pa_cache_store call are distinct;
+ *       * no store targets a block that several sequences share (a shared
+ *         block is copied before it is written, [mini-llm] §3.4);
+ *       * 0 <= context_lens[b] <= max_context_len <= max_blocks * block_size;
+ *       * positions[i] < max_pos for every token with slot_mapping[i] >= 0.
+ *   - Cache layout: k_cache and v_cache are bf16 [num_blocks][Hkv][block_size][D];
+ *     the 16 x D tile of one (block, KV head) is contiguous.  Token t of
+ *     sequence b lives in block block_tables[b][t / block_size], row
+ *     t % block_size ([mini-llm] §3.1, [nano-vllm] FAQ Q2).
+ *   - GQA: query head h reads KV head h / (Hq / Hkv) ([Pico-vLLM] §1).
+ *   - Supported shapes: block_size 16; head_dim 64 or 128; Hq % Hkv == 0 with
+ *     Hq / Hkv between 1 and 8.  Others return PA_ERR_UNSUPPORTED.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A hipStream_t.  NULL is the default (null) stream. */
+typedef void* pa_stream_t;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,         /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,        /* a size is negative, zero where it may not be, or inconsistent */
+  PA_ERR_UNSUPPORTED = 3,  /* consistent, but a shape this library does not implement */
+  PA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required */
+  PA_ERR_HIP = 5           /* the HIP runtime reported an error while enqueueing */
+} pa_status;
+
+/* Static, human-readable name of a status code.  Never NULL. */
+const char* pa_status_str(pa_status s);
+
+/*
+ * Fused rotate-half RoPE + KV-cache store ([Pico-vLLM] §2: position encoding
+ * fused with the cache write; §1: rotate_half computed in place; [mini-llm]
+ * §3.1: the slot of a token is a row of a physical block).
+ *
+ * For every token i in [0, T) with slot s = slot_mapping[i] >= 0 and position
+ * p = positions[i]:
+ *   k_cache[s / bs][g][s % bs][:] = bf16(rope(k[i][g][:], p))  for every KV head g
+ *   v_cache[s / bs][g][s % bs][:] = v[i][g][:]  (bits copied)  for every KV head g
+ *   q[i][h][:]                    = bf16(rope(q[i][h][:], p))  for every query head h (in place)
+ * A token with a negative slot is padding: nothing is read or written for it.
+ * rope pairs element j with element j + D/2 (j < D/2):
+ *   y[j]       = fl(fl(x[j] * c[j]) - fl(x[j + D/2] * s[j]))
+ *   y[j + D/2] = fl(fl(x[j + D/2] * c[j]) + fl(x[j] * s[j]))
+ * with c = cos_sin[p][0 .. D/2), s = cos_sin[p][D/2 .. D), every operation
+ * one fp32 IEEE operation rounded to nearest even (no fused multiply-add), and
+ * the result rounded to bf16 (nearest even).
+ *
+ * q            bf16 [T][Hq][D], rotated in place; may be NULL (then only k is rotated).
+ * k, v         bf16 [T][Hkv][D].
+ * k_cache, v_cache  bf16 [num_blocks][Hkv][block_size][D].
+ * slot_mapping int32 [T]; positions int32 [T].
+ * cos_sin      fp32 [max_pos][D]: cos of the D/2 angles, then their sin.
+ * T == 0 is a no-op that returns PA_OK.
+ */
+pa_status pa_cache_store(void* q, const void* k, const void* v, void* k_cache, void* v_cache,
+                         const int32_t* slot_mapping, const int32_t* positions,
+                         const float* cos_sin, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t block_size, int64_t num_blocks, int32_t max_pos,
+                         pa_stream_t stream);
+
+/*
+ * Bytes of workspace pa_decode needs for split-K decoding with this
+ * partition size: fp32 partial outputs [B][Hq][P][D] followed by fp32
+ * log-sum-exps [B][Hq][P], P = ceil(max_context_len / partition_size).
+ * partition_size 0 (single pass) needs none; -1 sizes the library's own
+ * choice (pa_decode_partition_size).  Returns 0 for invalid arguments.
+ */
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/*
+ * The partition size pa_decode uses when asked to choose (partition_size
+ * -1): 0 (single pass) when B * Hkv alone fills the GPU, otherwise a multiple
+ * of 16.  Host-only; reads the device's compute-unit count once.
+ */
+int32_t pa_decode_partition_size(int32_t B, int32_t Hkv, int32_t max_context_len);
+
+/*
+ * Paged GQA decode ([Pico-vLLM] §2 decode kernel with Flash-Attention-style
+ * tiling; Flash Decode in the H200 comparison; [mini-llm] §3.1):
+ *   out[b][h][:] = sum_{t < L_b} softmax_t(scale * q[b][h] . K_b[t][g]) V_b[t][g],
+ *   g = h / (Hq / Hkv), L_b = context_lens[b]; L_b == 0 gives zeros.
+ * The new token's K/V must already be in the cache (pa_cache_store) and q
+ * already rotated.  One workgroup serves all query heads of one KV head, so
+ * each K/V byte is read once per step.  Accumulation is fp32; out is rounded
+ * to bf16 (nearest even).
+ *
+ * out, q          bf16 [B][Hq][D]; out may not alias q.
+ * block_tables    int32 [B][max_blocks]; entries past ceil(L_b/16) are never read.
+ * context_lens    int32 [B].
+ * max_context_len host-known bound on context_lens (sizes the grid; no
+ *                 device-to-host read).
+ * partition_size  0: one pass over each sequence; > 0: split-K (Flash
+ *                 Decode) with partitions of that many tokens (a multiple of
+ *                 16), combined by a log-sum-exp reduce; -1: library's choice.
+ * workspace       device memory of at least pa_decode_workspace_bytes(...)
+ *                 bytes when split-K is used (may be NULL otherwise).
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                    int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size, int32_t max_blocks,
+                    int32_t max_context_len, float scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
+ * The two stages of split-K decode, for callers that place or exchange the
+ * partials themselves (e.g. partials computed on several devices for
+ * disjoint token ranges and combined on one).  pa_decode with
+ * partition_size > 0 is exactly pa_decode_partitions followed by
+ * pa_decode_combine on the same workspace.
+ *
+ * pa_decode_partitions: partition p of sequence b covers tokens
+ * [p*P, min((p+1)*P, L_b)).  For every non-empty partition it writes
+ *   o_part[b][h][p][:] = sum_t e^(s_t - m) V[t] / sum_t e^(s_t - m)   (fp32)
+ *   lse[b][h][p]       = log2(sum_t 2^(s_t*log2(e)))                  (fp32, base 2)
+ * with s_t = scale * q[b][h] . K[t][g].  Partitions with p*P >= L_b are not
+ * written.  o_part is [B][Hq][num_partitions][D] and lse is
+ * [B][Hq][num_partitions], num_partitions = ceil(max_context_len / P).
+ *
+ * pa_decode_combine: for every (b, h) with L_b > 0 and n = ceil(L_b / P),
+ *   M = max_{p<n} lse_p, w_p = 2^(lse_p - M),
+ *   out[b][h][:] = bf16(sum_p w_p o_part_p / sum_p w_p);
+ * L_b == 0 gives zeros.
+ */
+pa_status pa_decode_partitions(float* o_part, float* lse, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                               int32_t D, int32_t block_size, int32_t max_blocks,
+                               int32_t max_context_len, float scale, int32_t partition_size,
+                               pa_stream_t stream);
+
+pa_status pa_decode_combine(void* out, const float* o_part, const float* lse,
+                            const int32_t* context_lens, int32_t B, int32_t Hq, int32_t D,
+                            int32_t max_context_len, int32_t partition_size, pa_stream_t stream);
+
+/*
+ * Causal paged chunked prefill ([Pico-vLLM] §2 prefill kernel; [mini-llm]
+ * §3.3 Chunked Prefill).  Sequence b owns query rows
+ * [query_start_loc[b], query_start_loc[b+1]) (C_b rows) and has
+ * L_b = context_lens[b] cached tokens, its chunk's own keys included (store
+ * the chunk with pa_cache_store first).  Row i of the chunk sits at position
+ * L_b - C_b + i and attends keys t <= L_b - C_b + i:
+ *   out[r][h][:] = sum_t softmax_t(scale * q[r][h] . K_b[t][g]) V_b[t][g].
+ * QK^T and PV run on bf16 matrix cores with fp32 accumulation; out is
+ * rounded to bf16 (nearest even).
+ *
+ * out, q           bf16 [T][Hq][D] packed by sequence; out may not alias q.
+ * query_start_loc  int32 [B+1], non-decreasing, query_start_loc[B] == T,
+ *                  C_b <= L_b.
+ * max_query_len    host-known bound on C_b (sizes the grid).
+ */
+pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     const int32_t* query_start_loc, int32_t B, int32_t T, int32_t Hq, int32_t Hkv,
+                     int32_t D, int32_t block_size, int32_t max_blocks, int32_t max_query_len,
+                     float scale, pa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,202 @@
+// C ABI of libpa: argument validation, partition choice, workspace sizing and
+// dispatch to the gfx950 kernels.  Every check runs on the host before any
+// work is enqueued; nothing here allocates, synchronises or throws.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace pa {
+constexpr int kBlockSizeHost = 16;  // the only block size the kernels implement
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+bool head_shape_ok(int32_t Hq, int32_t Hkv, int32_t D, pa_status* st) {
+  if (Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) {
+    *st = PA_ERR_SHAPE;
+    return false;
+  }
+  const int32_t G = Hq / Hkv;
+  if ((D != 64 && D != 128) || G > 8) {
+    *st = PA_ERR_UNSUPPORTED;
+    return false;
+  }
+  return true;
+}
+
+pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Validation shared by the decode entry points.
+pa_status check_decode(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                       int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size, int32_t max_blocks,
+                       int32_t max_context_len) {
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  pa_status st = PA_OK;
+  if (!head_shape_ok(Hq, Hkv, D, &st)) return st;
+  if (block_size != pa::kBlockSizeHost) return block_size > 0 ? PA_ERR_UNSUPPORTED : PA_ERR_SHAPE;
+  if (B < 0 || max_blocks <= 0 || max_context_len < 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_context_len > (int64_t)max_blocks * block_size) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+int32_t resolve_partition(int32_t partition_size, int32_t B, int32_t Hkv, int32_t max_context_len) {
+  return partition_size == -1 ? pa_decode_partition_size(B, Hkv, max_context_len) : partition_size;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: sizes are inconsistent or out of range";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape not implemented (block_size 16, head_dim 64/128, Hq/Hkv <= 8)";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown pa_status";
+}
+
+pa_status pa_cache_store(void* q, const void* k, const void* v, void* k_cache, void* v_cache,
+                         const int32_t* slot_mapping, const int32_t* positions,
+                         const float* cos_sin, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t block_size, int64_t num_blocks, int32_t max_pos,
+                         pa_stream_t stream) {
+  if (T < 0 || num_blocks < 0 || max_pos < 0) return PA_ERR_SHAPE;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping || !positions || !cos_sin)
+    return PA_ERR_NULL;
+  pa_status st = PA_OK;
+  if (!head_shape_ok(q ? Hq : Hkv, Hkv, D, &st)) return st;
+  if (block_size != pa::kBlockSizeHost) return block_size > 0 ? PA_ERR_UNSUPPORTED : PA_ERR_SHAPE;
+  if (T == 0) return PA_OK;
+  if (num_blocks == 0 || max_pos == 0) return PA_ERR_SHAPE;
+  return from_hip(pa::launch_cache_store(q, k, v, k_cache, v_cache, slot_mapping, positions,
+                                         cos_sin, T, Hq, Hkv, D,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode_partition_size(int32_t B, int32_t Hkv, int32_t max_context_len) {
+  if (B <= 0 || Hkv <= 0 || max_context_len <= 0) return 0;
+  const int64_t target = 2LL * device_cu_count();  // workgroups to fill the GPU twice over
+  const int64_t pairs = (int64_t)B * Hkv;
+  if (pairs >= target) return 0;
+  const int64_t parts = ceil_div(target, pairs);
+  int64_t P = ceil_div(ceil_div(max_context_len, parts), 16) * 16;
+  if (P < 64) P = 64;
+  if (P > 512) P = 512;
+  if (P >= max_context_len) return 0;
+  return (int32_t)P;
+}
+
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t max_context_len, int32_t partition_size) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_context_len < 0) return 0;
+  const int32_t P = resolve_partition(partition_size, B, Hkv, max_context_len);
+  if (P <= 0 || P % 16 != 0) return 0;
+  const int64_t np = ceil_div(max_context_len, P);
+  return (size_t)((int64_t)B * Hq * np * (D + 1) * (int64_t)sizeof(float));
+}
+
+pa_status pa_decode_partitions(float* o_part, float* lse, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                               int32_t D, int32_t block_size, int32_t max_blocks,
+                               int32_t max_context_len, float scale, int32_t partition_size,
+                               pa_stream_t stream) {
+  if (!o_part || !lse) return PA_ERR_NULL;
+  pa_status st = check_decode(q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, D,
+                              block_size, max_blocks, max_context_len);
+  if (st != PA_OK) return st;
+  if (partition_size <= 0 || partition_size % 16 != 0) return PA_ERR_SHAPE;
+  if (B == 0 || max_context_len == 0) return PA_OK;
+  return from_hip(pa::launch_decode(nullptr, o_part, lse, q, k_cache, v_cache, block_tables,
+                                    context_lens, B, Hq, Hkv, D, max_blocks, max_context_len, scale,
+                                    partition_size, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_decode_combine(void* out, const float* o_part, const float* lse,
+                            const int32_t* context_lens, int32_t B, int32_t Hq, int32_t D,
+                            int32_t max_context_len, int32_t partition_size, pa_stream_t stream) {
+  if (!out || !o_part || !lse || !context_lens) return PA_ERR_NULL;
+  if (B < 0 || Hq <= 0 || max_context_len < 0) return PA_ERR_SHAPE;
+  if (D != 64 && D != 128) return D > 0 ? PA_ERR_UNSUPPORTED : PA_ERR_SHAPE;
+  if (partition_size <= 0 || partition_size % 16 != 0) return PA_ERR_SHAPE;
+  if (B == 0) return PA_OK;
+  const int np = (int)ceil_div(max_context_len, partition_size);
+  return from_hip(pa::launch_decode_combine(out, o_part, lse, context_lens, B, Hq, D,
+                                            np > 0 ? np : 1, partition_size,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                    int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size, int32_t max_blocks,
+                    int32_t max_context_len, float scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  if (!out) return PA_ERR_NULL;
+  pa_status st = check_decode(q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, D,
+                              block_size, max_blocks, max_context_len);
+  if (st != PA_OK) return st;
+  if (partition_size < -1 || (partition_size > 0 && partition_size % 16 != 0)) return PA_ERR_SHAPE;
+  const int32_t P = resolve_partition(partition_size, B, Hkv, max_context_len);
+  if (B == 0) return PA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (P == 0 || max_context_len == 0)
+    return from_hip(pa::launch_decode(out, nullptr, nullptr, q, k_cache, v_cache, block_tables,
+                                      context_lens, B, Hq, Hkv, D, max_blocks, max_context_len,
+                                      scale, 0, s));
+  const size_t need = pa_decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, P);
+  if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  const int64_t np = ceil_div(max_context_len, P);
+  float* o_part = static_cast<float*>(workspace);
+  float* lse = o_part + (int64_t)B * Hq * np * D;
+  hipError_t e = pa::launch_decode(nullptr, o_part, lse, q, k_cache, v_cache, block_tables,
+                                   context_lens, B, Hq, Hkv, D, max_blocks, max_context_len, scale,
+                                   P, s);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  return from_hip(pa::launch_decode_combine(out, o_part, lse, context_lens, B, Hq, D, (int)np, P, s));
+}
+
+pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     const int32_t* query_start_loc, int32_t B, int32_t T, int32_t Hq, int32_t Hkv,
+                     int32_t D, int32_t block_size, int32_t max_blocks, int32_t max_query_len,
+                     float scale, pa_stream_t stream) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
+    return PA_ERR_NULL;
+  pa_status st = PA_OK;
+  if (!head_shape_ok(Hq, Hkv, D, &st)) return st;
+  if (block_size != pa::kBlockSizeHost) return block_size > 0 ? PA_ERR_UNSUPPORTED : PA_ERR_SHAPE;
+  if (B < 0 || T < 0 || max_blocks <= 0 || max_query_len < 0) return PA_ERR_SHAPE;
+  if (B == 0 || T == 0 || max_query_len == 0) return PA_OK;
+  if (max_query_len > T) return PA_ERR_SHAPE;
+  return from_hip(pa::launch_prefill(out, q, k_cache, v_cache, block_tables, context_lens,
+                                     query_start_loc, B, Hq, Hkv, D, max_blocks, max_query_len,
+                                     scale, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// Internal launchers of libpa (C++ linkage, not part of the ABI).  Arguments
+// are already validated by the entry points in pa_api.cpp; each launcher only
+// picks the kernel instance and grid, enqueues it and reports the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+hipError_t launch_cache_store(void* q, const void* k, const void* v, void* k_cache, void* v_cache,
+                              const int32_t* slot_mapping, const int32_t* positions,
+                              const float* cos_sin, int T, int Hq, int Hkv, int D,
+                              hipStream_t stream);
+
+// Split-K partial kernel (partition_size > 0) or single pass (partition_size == 0,
+// o_part/lse unused, out written).
+hipError_t launch_decode(void* out, float* o_part, float* lse, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, int B, int Hq, int Hkv, int D,
+                         int max_blocks, int max_context_len, float scale, int partition_size,
+                         hipStream_t stream);
+
+hipError_t launch_decode_combine(void* out, const float* o_part, const float* lse,
+                                 const int32_t* context_lens, int B, int Hq, int D,
+                                 int num_partitions, int partition_size, hipStream_t stream);
+
+hipError_t launch_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          const int32_t* query_start_loc, int B, int Hq, int Hkv, int D,
+                          int max_blocks, int max_query_len, float scale, hipStream_t stream);
+
+}  // namespace pa

@@ -21,3 +21,9 @@ def gpu():
     import paged_kv_cache_240_amd as pa
     pa.load()  # raises if libpa.so is missing: there is no fallback
     return pa
+
+
+def pytest_runtest_logstart(nodeid, location):
+    """Name each test before it runs (flushed), so a GPU fault names its case."""
+    sys.stderr.write(f"\n>>> {nodeid}\n")
+    sys.stderr.flush()
