@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace pa {
 
 constexpr int kBlockSize = 16;  // tokens per physical KV block
@@ -26,6 +29,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Interleave two packed bf16 pairs: (a.lo, b.lo) and (a.hi, b.hi).
+__device__ __forceinline__ uint32_t interleave_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t interleave_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// A zero the compiler cannot see through.  Adding it to a base pointer inside
+// a loop keeps constant offsets from that base inside the loop, where they fold
+// into the memory instruction's immediate offset (hoisted, each offset would
+// hold a register of its own for the whole loop).
+__device__ __forceinline__ int opaque_zero() {
+  int z = 0;
+  asm volatile("; opaque zero" : "+s"(z));
+  return z;
+}
+
+// Wave-uniform float into a scalar register.
+__device__ __forceinline__ float uniform(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
 // a.x*b.x + a.y*b.y + c on two packed bf16 pairs (v_dot2_f32_bf16).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -41,16 +67,66 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+// Sum over the 8 lanes of an aligned octet, result in every lane: two quad
+// adds, then row_half_mirror (lane i of the octet reads lane 7-i), which pairs
+// each lane of one quad with a lane of the other.
+__device__ __forceinline__ float octet_sum(float x) {
+  x = quad_sum(x);
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                             0x141, 0xF, 0xF, false));
   return x;
 }
 
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1: a loop whose
+// index is a compile-time constant in the body (register arrays stay in
+// registers however large the body is).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Cross-lane partners without LDS: DPP inside 16-lane rows, then the gfx950
+// row swaps (v_permlane16_swap: rows 0<->1 and 2<->3; v_permlane32_swap:
+// lanes 0-31 <-> 32-63).  Each returns, in every lane, the value its partner
+// row holds in the same position.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+__device__ __forceinline__ float swap16(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  // r[0]: own value in even rows, partner's in odd rows; r[1]: the reverse
+  return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float swap32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// Reductions over the 64 lanes of a wave, result in every lane.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp<0x140>(x));  // row_mirror
+  x = fmaxf(x, swap16(x));
+  return fmaxf(x, swap32(x));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  x += swap16(x);
+  return x + swap32(x);
 }
 
 }  // namespace pa
