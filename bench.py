@@ -1,0 +1,386 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+
+Headline workload (the long-context flash-decode): 16 sequences x 8192 cached
+tokens, 12 query / 2 KV heads (the Qwen2.5-1.5B attention shape), head_dim
+128, 16-token blocks, split-K partitions of 512 tokens, 28 independent layer
+caches run back to back (3.76 GB of K/V, far beyond the 256 MB last-level
+cache, so every step reads HBM).  One step = for each of the 28 layers:
+fused RoPE + KV-cache store of the step's 16 new tokens, the split-K
+partition kernel, the log-sum-exp combine (pa_decode with partition_size 512
+is exactly the last two).  All inputs are synthetic, seeded, resident in HBM.
+
+Printed: one JSON line.  value = effective KV GB/s of the whole step (K/V
+bytes the 28 layers read / step time).  roofline = the partition kernel
+(dominant) timed per launch with HIP events on its stream, against 8 TB/s.
+cpu_baseline = the CPU oracle on a bounded sample of the same workload.
+Extra keys: decode-only rates, the batch-1 2048-token decode call, the
+continuous-batching step, and the chunked prefill.
+
+Other modes (for profiling with rocprofv3, committed so profile commands run
+committed files only):
+    python bench.py --mode decode-kernel   # 3 x 28 launches of the partition kernel only
+    python bench.py --mode prefill-kernel  # 20 launches of the prefill kernel only
+    python bench.py --mode copy-calibration  # torch copy of 1 GiB (FETCH/WRITE_SIZE scale)
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import paged_kv_cache_240_amd as pa  # noqa: E402
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+LONG_P = W.LONG_PARTITION
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def _event():
+    return torch.cuda.Event(enable_timing=True)
+
+
+def kernel_source_hash(name):
+    with open(os.path.join(ROOT, "paged_kv_cache_240_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# Workload set-up
+# ---------------------------------------------------------------------------
+
+def make_long_layers(layers, device):
+    """The layer caches with their library calls prepared once (validated and
+    marshalled; each call then costs one C call, as in a serving loop)."""
+    out = []
+    for layer in range(layers):
+        b = W.long_decode_layer(layer, device=device)
+        P = LONG_P
+        np_ = -(-b.max_context_len // P)
+        o_part = torch.empty((b.B, b.Hq, np_, b.D), dtype=torch.float32, device=device)
+        lse = torch.empty((b.B, b.Hq, np_), dtype=torch.float32, device=device)
+        dout = torch.empty((b.B, b.Hq, b.D), dtype=torch.bfloat16, device=device)
+        b.meta["store"] = pa.prepare_cache_store(b.q, b.k, b.v, b.k_cache, b.v_cache,
+                                                 b.slot_mapping, b.positions, b.cos_sin)
+        b.meta["partitions"] = pa.prepare_decode_partitions(b.q, b.k_cache, b.v_cache, b.block_tables,
+                                                            b.context_lens, b.scale, b.max_context_len,
+                                                            P, o_part, lse)
+        b.meta["combine"] = pa.prepare_decode_combine(o_part, lse, b.context_lens, b.max_context_len,
+                                                      P, dout)
+        out.append(b)
+    return out
+
+
+def store(b):
+    b.meta["store"]()
+
+
+def partitions(b):
+    b.meta["partitions"]()
+
+
+def combine(b):
+    b.meta["combine"]()
+
+
+def partition_kernel_bytes(b):
+    """Algorithmic bytes one partition-kernel launch must read: K and V of every
+    context token, the queries, the block table and the context lengths."""
+    kv = W.kv_bytes_logical(b.context_lens.cpu().numpy(), b.Hkv, b.D)
+    return kv + b.q.numel() * 2 + b.B * (-(-b.max_context_len // 16)) * 4 + b.B * 4
+
+
+# ---------------------------------------------------------------------------
+# Headline: long-context decode steps
+# ---------------------------------------------------------------------------
+
+def run_long(layers, steps, warmup):
+    L = layers
+
+    def step(evs=None):
+        for i, b in enumerate(L):
+            store(b)
+            if evs is not None:
+                evs[i][0].record()
+            partitions(b)
+            if evs is not None:
+                evs[i][1].record()
+            combine(b)
+
+    for _ in range(warmup):
+        step()
+    _sync()
+    ev = [[[_event(), _event()] for _ in L] for _ in range(steps)]
+    t0, t1 = _event(), _event()
+    _sync()
+    t0.record()
+    for s in range(steps):
+        step(ev[s])
+    t1.record()
+    _sync()
+    step_ms = t0.elapsed_time(t1) / steps
+    part_us = [ev[s][i][0].elapsed_time(ev[s][i][1]) * 1000 for s in range(steps) for i in range(len(L))]
+
+    # decode only (partitions + combine), same data, for context
+    d0, d1 = _event(), _event()
+    d0.record()
+    for _ in range(steps):
+        for b in L:
+            partitions(b)
+            combine(b)
+    d1.record()
+    _sync()
+    decode_only_ms = d0.elapsed_time(d1) / steps
+    return step_ms, float(np.mean(part_us)), float(np.median(part_us)), decode_only_ms
+
+
+# ---------------------------------------------------------------------------
+# Context measurements (the other decode shapes and the prefill)
+# ---------------------------------------------------------------------------
+
+def time_calls(fn, reps, warm=10):
+    for _ in range(warm):
+        fn()
+    _sync()
+    e0, e1 = _event(), _event()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    _sync()
+    return e0.elapsed_time(e1) * 1000 / reps
+
+
+def run_context(device):
+    res = {}
+    # batch 1, 2048 tokens: store + decode, library-chosen partitions, warm
+    b = W.qwen_decode(device=device)
+    P = pa.decode_partition_size(b.B, b.Hkv, b.max_context_len)
+    dec = pa.prepare_decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale,
+                            b.max_context_len, partition_size=P)
+    st = pa.prepare_cache_store(b.q, b.k, b.v, b.k_cache, b.v_cache, b.slot_mapping, b.positions,
+                                b.cos_sin)
+
+    def step2():
+        st()
+        dec()
+
+    us = time_calls(dec, 1000)
+    res["qwen_b1_l2048"] = {"decode_us_per_call": round(us, 2), "partition_size": P,
+                            "store_plus_decode_us": round(time_calls(step2, 1000), 2),
+                            "kv_GBps": round(W.kv_bytes_logical([2048], 2, 128) / us / 1e3, 1)}
+    # continuous-batching step: 64 sequences, 32 share a 2000-token prefix
+    b = W.cb_step(device=device)
+    P = pa.decode_partition_size(b.B, b.Hkv, b.max_context_len)
+    dec3 = pa.prepare_decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale,
+                             b.max_context_len, partition_size=P)
+
+    us = time_calls(dec3, 200)
+    lens = b.context_lens.cpu().numpy()
+    logical = W.kv_bytes_logical(lens, 2, 128)
+    unique = W.kv_bytes_unique(b.block_tables.cpu().numpy(), lens, 2, 128)
+    res["cb_step_b64"] = {"decode_us_per_call": round(us, 2), "partition_size": P,
+                          "kv_logical_GBps": round(logical / us / 1e3, 1),
+                          "kv_unique_GBps_warm": round(unique / us / 1e3, 1),
+                          "note": "warm: 28.5 MB of unique K/V stays in the last-level cache"}
+    # chunked prefill: 4 x (2048 cached + 512 new), store then prefill
+    b = W.chunked_prefill(device=device)
+    pst = pa.prepare_cache_store(b.q, b.k, b.v, b.k_cache, b.v_cache, b.slot_mapping, b.positions,
+                                 b.cos_sin)
+    pre = pa.prepare_prefill(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
+                             b.query_start_loc, b.scale, b.max_query_len)
+    pst()
+    us_pre = time_calls(pre, 50)
+    us_store = time_calls(pst, 50)
+    flops = prefill_flops(b)
+    res["chunked_prefill"] = {"prefill_us": round(us_pre, 2), "store_us": round(us_store, 2),
+                              "prefill_TFLOPs": round(flops / us_pre / 1e6, 1),
+                              "mfma_bf16_frac": round(flops / us_pre / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "flop": flops}
+    return res
+
+
+def prefill_flops(b):
+    """4 * D multiply-adds... per visible (row, key) pair: QK^T and PV, 2 flop each."""
+    qsl = b.query_start_loc.cpu().numpy()
+    lens = b.context_lens.cpu().numpy()
+    pairs = 0
+    for s in range(b.B):
+        C, L = int(qsl[s + 1] - qsl[s]), int(lens[s])
+        pairs += sum(L - C + i + 1 for i in range(C))
+    return pairs * b.Hq * 4 * b.D
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the headline workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(layers, budget_s):
+    import oracle  # test infrastructure; used here only for the CPU baseline leg
+    from workloads import as_bits
+    done_bytes = 0
+    seqs = 0
+    t_total = 0.0
+    threads = torch.get_num_threads()
+    for b in layers:
+        kc, vc = as_bits(b.k_cache), as_bits(b.v_cache)
+        bt = b.block_tables.cpu().numpy()
+        cl = b.context_lens.cpu().numpy()
+        qb = as_bits(b.q)
+        for s in range(b.B):
+            t0 = time.perf_counter()
+            oracle.decode(qb[s:s + 1], kc, vc, bt[s:s + 1], cl[s:s + 1], b.scale)
+            t_total += time.perf_counter() - t0
+            done_bytes += W.kv_bytes_logical(cl[s:s + 1], b.Hkv, b.D)
+            seqs += 1
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle decode of {seqs} (sequence, layer) pairs of the "
+                      f"long-context workload (8192 tokens x 2 KV heads each), {t_total:.1f} s"}
+
+
+def load_traffic(kernel_file, kernel_name):
+    """HBM bytes per launch measured with rocprofv3 counters, if taken on the current kernel."""
+    path = os.path.join(ROOT, "profiles", "decode_partitions_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != kernel_source_hash(kernel_file) or rec.get("kernel") != kernel_name:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=W.LONG_LAYERS)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true")
+    ap.add_argument("--mode", default="bench",
+                    choices=["bench", "decode-kernel", "prefill-kernel", "copy-calibration"])
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence or KV head with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    pa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.mode == "copy-calibration":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        _sync()
+        for _ in range(3):
+            dst.copy_(src)
+        _sync()
+        print(json.dumps({"mode": "copy-calibration", "bytes_read": n, "bytes_written": n}))
+        return
+    if args.mode == "decode-kernel":
+        Ls = make_long_layers(args.layers, dev)
+        _sync()
+        for _ in range(3):
+            for b in Ls:
+                partitions(b)
+        _sync()
+        print(json.dumps({"mode": "decode-kernel", "launches": 3 * len(Ls),
+                          "bytes_per_launch": partition_kernel_bytes(Ls[0])}))
+        return
+    if args.mode == "prefill-kernel":
+        b = W.chunked_prefill(device=dev)
+        pa.cache_store(b.q, b.k, b.v, b.k_cache, b.v_cache, b.slot_mapping, b.positions, b.cos_sin)
+        pre = pa.prepare_prefill(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
+                                 b.query_start_loc, b.scale, b.max_query_len)
+        for _ in range(20):
+            pre()
+        _sync()
+        print(json.dumps({"mode": "prefill-kernel", "launches": 20, "flop_per_launch": prefill_flops(b)}))
+        return
+
+    layers = make_long_layers(args.layers, dev)
+    _sync()
+    step_ms, part_avg_us, part_med_us, decode_only_ms = run_long(layers, args.steps, args.warmup)
+    kv_step = sum(W.kv_bytes_logical(b.context_lens.cpu().numpy(), b.Hkv, b.D) for b in layers)
+    value = kv_step / (step_ms * 1e-3) / 1e9
+    launch_bytes = partition_kernel_bytes(layers[0])
+    achieved = launch_bytes / (part_avg_us * 1e-6) / 1e9
+    traffic = load_traffic("k_decode.hip", "decode_kernel<128, 6, true, true>")
+    line = {
+        "metric": "paged-attn decode effective KV GB/s (% of HBM peak); us/call at Qwen2.5-1.5B shape",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "long-context flash-decode step: 28 layer caches x (RoPE+store of 16 new "
+                        "tokens, split-K decode, LSE combine)",
+            "batch": layers[0].B, "context_len": layers[0].max_context_len,
+            "q_heads": layers[0].Hq, "kv_heads": layers[0].Hkv, "head_dim": layers[0].D,
+            "block_size": 16, "partition_size": LONG_P, "layers": len(layers),
+            "kv_bytes_per_step": kv_step,
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "us_per_layer_call": round(step_ms * 1000 / len(layers), 2),
+        "decode_only": {"us_per_layer_call": round(decode_only_ms * 1000 / len(layers), 2),
+                        "kv_GBps": round(kv_step / (decode_only_ms * 1e-3) / 1e9, 1)},
+        "roofline": {
+            "kernel": "decode_kernel<128, 6, true, true> (split-K partitions)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": launch_bytes,
+            "avg_launch_us": round(part_avg_us, 3),
+            "median_launch_us": round(part_med_us, 3),
+        },
+    }
+    if not args.no_context:
+        line["context"] = run_context(dev)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(layers, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

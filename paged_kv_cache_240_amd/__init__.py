@@ -19,9 +19,11 @@ import os
 
 import torch
 
-__all__ = ["load", "PAError", "cache_store", "decode", "decode_partitions", "decode_combine",
-           "decode_workspace_bytes", "decode_partition_size", "prefill", "BLOCK_SIZE",
-           "library_path", "STATUS"]
+__all__ = ["load", "PAError", "Call", "cache_store", "decode", "decode_partitions",
+           "decode_combine", "prefill", "prepare_cache_store", "prepare_decode",
+           "prepare_decode_partitions", "prepare_decode_combine", "prepare_prefill",
+           "decode_workspace_bytes", "decode_partition_size", "BLOCK_SIZE", "library_path",
+           "STATUS"]
 
 BLOCK_SIZE = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,10 +79,28 @@ def load():
     return _lib
 
 
-def _call(name, *args):
-    st = getattr(load(), name)(*args)
-    if st != 0:
-        raise PAError(name, st)
+class Call:
+    """One library call, validated and marshalled once.
+
+    Calling the object enqueues the operation again with the same pointers,
+    sizes and stream (no per-call Python checks), e.g. once per decode step
+    while the tensors stay in place.  `result` is what the call writes.
+    """
+
+    __slots__ = ("name", "fn", "args", "result", "keep")
+
+    def __init__(self, name, args, result=None, keep=()):
+        self.name = name
+        self.fn = getattr(load(), name)
+        self.args = args
+        self.result = result
+        self.keep = keep  # the tensors whose pointers are in args stay alive with the call
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise PAError(self.name, st)
+        return self.result
 
 
 def _ptr(t):
@@ -123,6 +143,11 @@ def cache_store(q, k, v, k_cache, v_cache, slot_mapping, positions, cos_sin):
     q bf16 [T, Hq, D] or None; k, v bf16 [T, Hkv, D]; caches bf16 [NB, Hkv, 16, D];
     slot_mapping, positions int32 [T]; cos_sin float32 [max_pos, D].
     """
+    prepare_cache_store(q, k, v, k_cache, v_cache, slot_mapping, positions, cos_sin)()
+
+
+def prepare_cache_store(q, k, v, k_cache, v_cache, slot_mapping, positions, cos_sin):
+    """Validated pa_cache_store call (see cache_store) on the current stream."""
     nb, hkv, bs, d = _cache_dims(k_cache, v_cache)
     dev = k_cache.device
     _check(k, "k", torch.bfloat16, 3, dev)
@@ -143,9 +168,10 @@ def cache_store(q, k, v, k_cache, v_cache, slot_mapping, positions, cos_sin):
     _check(cos_sin, "cos_sin", torch.float32, 2, dev)
     if cos_sin.shape[1] != d:
         raise ValueError("cos_sin must be [max_pos, D]")
-    _call("pa_cache_store", _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
-          _ptr(slot_mapping), _ptr(positions), _ptr(cos_sin), T, hq, hkv, d, bs, nb,
-          cos_sin.shape[0], _stream(dev))
+    return Call("pa_cache_store", (_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(slot_mapping), _ptr(positions), _ptr(cos_sin), T, hq, hkv,
+                                   d, bs, nb, cos_sin.shape[0], _stream(dev)),
+                keep=(q, k, v, k_cache, v_cache, slot_mapping, positions, cos_sin))
 
 
 def decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, partition_size=-1):
@@ -177,6 +203,13 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_l
     max_context_len must bound context_lens (it sizes the grid).  partition_size:
     0 single pass, >0 split-K with that many tokens per partition, -1 library's choice.
     """
+    return prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                          partition_size, out, workspace)()
+
+
+def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                   partition_size=-1, out=None, workspace=None):
+    """Validated pa_decode call (see decode); allocates out/workspace once."""
     dev, B, hq, hkv, d, bs, mb = _decode_common(q, k_cache, v_cache, block_tables, context_lens)
     if out is None:
         out = torch.empty_like(q)
@@ -190,10 +223,10 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_l
     if workspace is not None:
         _check(workspace, "workspace", workspace.dtype, None, dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _call("pa_decode", _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-          _ptr(context_lens), B, hq, hkv, d, bs, mb, int(max_context_len), float(scale), P,
-          _ptr(workspace), wbytes, _stream(dev))
-    return out
+    return Call("pa_decode", (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                              _ptr(context_lens), B, hq, hkv, d, bs, mb, int(max_context_len),
+                              float(scale), P, _ptr(workspace), wbytes, _stream(dev)),
+                result=out, keep=(q, k_cache, v_cache, block_tables, context_lens, workspace))
 
 
 def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
@@ -203,6 +236,13 @@ def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, ma
     Returns (o_part fp32 [B, Hq, NP, D], lse fp32 [B, Hq, NP]), NP = ceil(max_context_len / P);
     entries of empty partitions are left as they were.
     """
+    return prepare_decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale,
+                                     max_context_len, partition_size, o_part, lse)()
+
+
+def prepare_decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale,
+                              max_context_len, partition_size, o_part=None, lse=None):
+    """Validated pa_decode_partitions call (see decode_partitions)."""
     dev, B, hq, hkv, d, bs, mb = _decode_common(q, k_cache, v_cache, block_tables, context_lens)
     P = int(partition_size)
     if P <= 0:
@@ -216,14 +256,20 @@ def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, ma
     _check(lse, "lse", torch.float32, 3, dev)
     if tuple(o_part.shape) != (B, hq, np_, d) or tuple(lse.shape) != (B, hq, np_):
         raise ValueError("o_part / lse have the wrong shape")
-    _call("pa_decode_partitions", _ptr(o_part), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-          _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, bs, mb, int(max_context_len),
-          float(scale), P, _stream(dev))
-    return o_part, lse
+    return Call("pa_decode_partitions",
+                (_ptr(o_part), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                 _ptr(context_lens), B, hq, hkv, d, bs, mb, int(max_context_len), float(scale), P,
+                 _stream(dev)),
+                result=(o_part, lse), keep=(q, k_cache, v_cache, block_tables, context_lens))
 
 
 def decode_combine(o_part, lse, context_lens, max_context_len, partition_size, out=None):
     """Second split-K stage (pa_decode_combine).  Returns out bf16 [B, Hq, D]."""
+    return prepare_decode_combine(o_part, lse, context_lens, max_context_len, partition_size, out)()
+
+
+def prepare_decode_combine(o_part, lse, context_lens, max_context_len, partition_size, out=None):
+    """Validated pa_decode_combine call (see decode_combine)."""
     dev = o_part.device
     _check(o_part, "o_part", torch.float32, 4, dev)
     _check(lse, "lse", torch.float32, 3, dev)
@@ -236,14 +282,21 @@ def decode_combine(o_part, lse, context_lens, max_context_len, partition_size, o
     if out is None:
         out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
     _check(out, "out", torch.bfloat16, 3, dev)
-    _call("pa_decode_combine", _ptr(out), _ptr(o_part), _ptr(lse), _ptr(context_lens), B, hq, d,
-          int(max_context_len), int(partition_size), _stream(dev))
-    return out
+    return Call("pa_decode_combine", (_ptr(out), _ptr(o_part), _ptr(lse), _ptr(context_lens), B, hq,
+                                      d, int(max_context_len), int(partition_size), _stream(dev)),
+                result=out, keep=(o_part, lse, context_lens))
 
 
 def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
             max_query_len, out=None):
     """Causal paged chunked prefill (pa_prefill).  Returns out bf16 [T, Hq, D]."""
+    return prepare_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
+                           max_query_len, out)()
+
+
+def prepare_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
+                    max_query_len, out=None):
+    """Validated pa_prefill call (see prefill)."""
     nb, hkv, bs, d = _cache_dims(k_cache, v_cache)
     dev = k_cache.device
     _check(q, "q", torch.bfloat16, 3, dev)
@@ -259,7 +312,8 @@ def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, sc
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", torch.bfloat16, 3, dev)
-    _call("pa_prefill", _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-          _ptr(context_lens), _ptr(query_start_loc), B, T, hq, hkv, d, bs, block_tables.shape[1],
-          int(max_query_len), float(scale), _stream(dev))
-    return out
+    return Call("pa_prefill", (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                               _ptr(context_lens), _ptr(query_start_loc), B, T, hq, hkv, d, bs,
+                               block_tables.shape[1], int(max_query_len), float(scale),
+                               _stream(dev)),
+                result=out, keep=(q, k_cache, v_cache, block_tables, context_lens, query_start_loc))
