@@ -10,22 +10,23 @@
 //
 // Workgroup = 4 independent waves; the tokens of a partition (split-K) or of
 // the whole sequence (single pass) are walked in chunks of 32 blocks, wave w
-// taking blocks w, w+4, ..., w+28 of each chunk.  Per chunk each wave:
-//   QK   S^T = K Q^T for the 16 keys of a block and the G query heads (padded
-//        to 16) with v_mfma_f32_16x16x32_bf16: the key tile is the A operand
-//        as it lies in memory (lane = key, 16 contiguous bytes of its row per
-//        k-step), the query rows the B operand (16 registers whatever G).
-//        Each lane then holds 4 consecutive keys of one head; scaled by
-//        scale*log2 e (rows past the range set to -inf by a select), they go
-//        to the wave's LDS slice with one 16-byte store.
-//   P    the wave's running max/sum per head (online softmax across chunks,
-//        wave shuffles); p = 2^(s - m) is rounded to bf16 and stored as
-//        (even row, odd row) pairs in the order the PV step reads them.
-//   PV   lane (row group, 4 dims) takes 8-byte pieces of 16/TG rows of a V
-//        block (rows 2m and 2m+1 for its pairs m); v_perm interleaves the two
-//        rows per dim so v_dot2_f32_bf16 applies both probabilities at once,
-//        with fp32 accumulation.  Rows past the range are zeroed by a select,
-//        so NaN in unused slots never reaches a sum.
+// taking blocks w, w+4, ..., w+28 of each chunk.  Both products run on
+// v_mfma_f32_16x16x32_bf16 with the G query heads padded to 16:
+//   QK   S^T = K Q^T per block: the key tile is the A operand as it lies in
+//        memory (lane = key, 16 contiguous bytes of its row per k-step), the
+//        query rows the B operand.  A lane ends up with 4 consecutive keys of
+//        one head; rows past the range become -inf by a select.
+//   P    after the 8 blocks of a chunk, the running max per head (in-lane max,
+//        then two cross-row swaps: a head's 32 keys of a block pair live in
+//        4 lanes), p = 2^((s - m) * scale * log2 e), rounded to bf16 in place:
+//        the 8 p of a lane for two blocks are exactly its A operand of PV.
+//   PV   O = P V per block pair (32 keys): lane (n, g) loads rows 4g..4g+3 of
+//        each block, D/16 consecutive dims from n*D/16; v_perm pairs the rows
+//        per dim, which makes the B operand of the output tile holding dims
+//        n*D/16 + s.  A ninth product against a ones operand accumulates the
+//        normaliser l from the same rounded p the outputs use.
+// Rows past the range are redirected to row 0 of their block when V is
+// loaded, so NaN in unused slots never meets a zero probability.
 // K and V blocks stream through a ring of DEPTH register buffers in the
 // order K0..K7, V0..V7, K0' ... so loads run DEPTH blocks ahead of the
 // arithmetic across phase and chunk boundaries.  Loads past the last block of
@@ -34,9 +35,6 @@
 // triples are combined through LDS.  The output is the normalised bf16 row
 // (single pass) or an fp32 partial plus its base-2 log-sum-exp (split-K),
 // reduced by combine_kernel (Flash Decode's reduce).
-//
-// Block-table entries are read with wave-uniform addresses (scalar loads);
-// entries past the sequence's last block are never read.
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -52,12 +50,27 @@ constexpr int kWaves = 4;
 constexpr int kWaveBlocks = 8;                           // blocks per wave per chunk
 constexpr int kChunkBlocks = kWaves * kWaveBlocks;       // 32
 constexpr int kChunkTokens = kChunkBlocks * kBlockSize;  // 512
-constexpr int kWaveTokens = kWaveBlocks * kBlockSize;    // 128
 constexpr int kDepth = 4;     // blocks in flight per wave when chunks repeat (ring slots must cycle per chunk)
 constexpr int kDepthOne = PA_DECODE_DEPTH_ONE;  // ... when the range is a single chunk
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // two bf16 1.0
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4_t mfma_bf16(uint4 a, uint4 b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// 2^x on v_exp_f32 directly: results below the fp32 normal range may flush to
+// zero, which only touches probabilities already under 2^-126 of the maximum.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  const bf16x2_t r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
 
 // ONE: the range is a single chunk (split-K with partitions of at most 512
 // tokens), so the ring need not cycle and can be deeper; no refills past it.
@@ -68,24 +81,17 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
               const int32_t* __restrict__ context_lens, int Hkv, int max_blocks,
               float scale_log2, int part_tokens, int num_parts, uint16_t* __restrict__ out,
               float* __restrict__ o_part, float* __restrict__ lse) {
-  static_assert(G >= 1 && G <= 16, "query heads per KV head must fit the 16 MFMA columns");
-  constexpr int KS = D / 32;          // MFMA k-steps over the head dimension
-  constexpr int VL = D / 4;           // lanes per row in the PV layout (4 dims each)
-  constexpr int TG = 64 / VL;         // row groups in the PV layout
-  constexpr int NPAIR = 8 / TG;       // row pairs per lane per block
-  constexpr int SLOT = 4 * KS;        // dwords per lane of a K block (16 bytes per k-step)
-  static_assert(SLOT == 4 * NPAIR, "K and V blocks must occupy the same ring slot");
+  static_assert(G >= 1 && G <= 8, "query heads per KV head: 1..8");
+  constexpr int KS = D / 32;    // QK k-steps over the head dimension
+  constexpr int DPL = D / 16;   // PV: dims per lane = output tiles of 16 columns
+  constexpr int HALF = DPL / 2; // dwords of one V row piece
+  constexpr int SLOT = 4 * KS;  // dwords per lane of a K block (16 bytes per k-step)
+  static_assert(SLOT == 4 * HALF, "K and V blocks must occupy the same ring slot");
   constexpr int STEPS = 2 * kWaveBlocks;  // K0..K7 then V0..V7
   constexpr int DEPTH = ONE ? kDepthOne : kDepth;
-  static_assert(ONE || STEPS % DEPTH == 0, "ring slots must repeat per chunk");
-  constexpr int S_WAVE = G * kWaveTokens;  // floats of one wave's score slice
-  static_assert(kWaves * S_WAVE >= G * D, "reduction buffer fits in the score slices");
+  static_assert(DEPTH % 2 == 0 && (ONE || STEPS % DEPTH == 0), "ring slots must repeat per chunk");
 
-  // Wave slice, head h, block i: 16 floats of scores in key order; after the P
-  // step its first 8 dwords hold bf16 probability pairs, pair m at
-  // (m % TG) * NPAIR + m / TG (the order a PV lane reads its NPAIR pairs).
-  __shared__ __align__(16) float s_buf[kWaves * S_WAVE];
-  __shared__ __align__(16) float s_junk[kWaves][64];  // stores of lanes whose head is >= G
+  __shared__ __align__(16) float red[kWaves][G][D];  // per-wave outputs, dim n*DPL+s at s*16+n
   __shared__ float st_m[kWaves][G], st_l[kWaves][G];
 
   const int lane = threadIdx.x & 63;
@@ -103,12 +109,12 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
   const int lb_spec = lb0 + wave + kWaves * (threadIdx.x & 7);
   const int ent_spec = bt_row[min(lb_spec, max_blocks - 1)];
   const int ent_first = bt_row[lb0];
-  const int col = threadIdx.x & 15, quad = (threadIdx.x >> 4) & 3;  // MFMA lane roles
-  // B operand: query row of head `col` (zero beyond G), 8 dims per k-step;
-  // padding lanes read head 0 and discard it (a select, not a branch)
-  uint4 qraw[D / 32];
+  const int col = lane & 15, quad = lane >> 4;  // MFMA lane roles
+  // B operand of QK: query row of head `col` (zero beyond G), 8 dims per
+  // k-step; padding lanes read head 0 and discard it (a select, not a branch)
+  uint4 qraw[KS];
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
+  for (int ks = 0; ks < KS; ++ks)
     qraw[ks] = *reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + hq0 + min(col, G - 1)) * D +
                                                ks * 32 + quad * 8);
   // every start-up load is in flight before the emptiness test below
@@ -125,29 +131,23 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
     return;
   }
 
-  const int tg = lane / VL, dq = lane % VL;  // PV layout: row group, 4-dim piece
-  bf16x8_t qb[KS];
+  uint4 qb[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qb[ks] = __builtin_bit_cast(bf16x8_t, col < G ? qraw[ks] : make_uint4(0u, 0u, 0u, 0u));
+  for (int ks = 0; ks < KS; ++ks) qb[ks] = col < G ? qraw[ks] : make_uint4(0u, 0u, 0u, 0u);
 
-  float acc[G][4];
-  float m_run[G], l_run[G];  // wave-uniform
+  floatx4_t o[DPL];  // O[head 4*quad+e][dim col*DPL+s] in o[s][e]
+  floatx4_t lacc = {0.f, 0.f, 0.f, 0.f};  // l of head 4*quad+e (every column the same)
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[h][e] = 0.f;
-  }
+  for (int s = 0; s < DPL; ++s) o[s] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // raw-score max of head `col` (same in the 4 lanes of a head)
 
-  float* sw = s_buf + wave * S_WAVE;
   const int64_t head_off = (int64_t)g * kBlockSize * D;
   const int64_t blk_stride = (int64_t)Hkv * kBlockSize * D;
   const int nchunks = ONE ? 1 : (t_end - t_begin + kChunkTokens - 1) / kChunkTokens;
   const int last_lb = (t_end - 1) / kBlockSize;  // last logical block of the range
   const int lane_k = col * D + quad * 8;         // element offsets inside a block tile
-  const int lane_v = 2 * tg * D + dq * 4;
+  const int lane_v = col * DPL;
+  const uint4 ones = make_uint4(kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2);
 
   // Block-table entries of this wave's 8 blocks of chunk c: one vector load,
   // lane j (mod 8) fetching the entry of block j; blocks past the range take
@@ -157,155 +157,143 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
     const int lb = (t_begin + c * kChunkTokens) / kBlockSize + wave + kWaves * (lane & 7);
     return bt_row[min(lb, last_lb)];
   };
-  // Ring step `step` (0..7 K blocks, 8..15 V blocks) of the chunk whose entries are `ent`.
-  auto load_step = [&](uint32_t (&slot)[SLOT], int ent, int step) {
+  // Ring step `step` (0..7 K blocks, 8..15 V blocks) of the chunk whose
+  // entries are `ent`; `left` = rows of that block inside the range.
+  auto load_step = [&](uint32_t (&slot)[SLOT], int ent, int step, int left) {
     const int i = step & (kWaveBlocks - 1);
     const int64_t base = (int64_t)__builtin_amdgcn_readlane(ent, i) * blk_stride + head_off;
     if (step < kWaveBlocks) {
       const uint16_t* src = k_cache + base + lane_k;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 t = *reinterpret_cast<const uint4*>(src + ks * 32);
+        const uint4 t = load_stream16(src + ks * 32);
         slot[4 * ks] = t.x; slot[4 * ks + 1] = t.y; slot[4 * ks + 2] = t.z; slot[4 * ks + 3] = t.w;
       }
     } else {
-      // pair k covers rows 2m, 2m+1 with m = tg + TG*k
       const uint16_t* src = v_cache + base + lane_v;
 #pragma unroll
-      for (int k = 0; k < NPAIR; ++k)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint2 t = *reinterpret_cast<const uint2*>(src + (2 * TG * k + e) * D);
-          slot[4 * k + 2 * e] = t.x; slot[4 * k + 2 * e + 1] = t.y;
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * quad + r < left ? 4 * quad + r : 0;  // past the range: row 0 (finite)
+        if constexpr (HALF == 4) {
+          const uint4 t = load_stream16(src + row * D);
+          slot[4 * r] = t.x; slot[4 * r + 1] = t.y; slot[4 * r + 2] = t.z; slot[4 * r + 3] = t.w;
+        } else {
+          const uint2 t = load_stream8(src + row * D);
+          slot[2 * r] = t.x; slot[2 * r + 1] = t.y;
         }
+      }
     }
   };
+  auto rows_left = [&](int nt, int step) { return nt - (wave + kWaves * (step & 7)) * kBlockSize; };
 
   int ent_cur = lb_spec <= last_lb ? ent_spec : ent_first;  // == fetch_entries(0)
   int ent_nxt = ONE ? 0 : fetch_entries(nchunks > 1 ? 1 : 0);
+  const int nt0 = min(kChunkTokens, t_end - t_begin);
   uint32_t ring[DEPTH][SLOT];
 #pragma unroll
-  for (int s = 0; s < DEPTH; ++s) load_step(ring[s], ent_cur, s);
+  for (int s = 0; s < DEPTH; ++s) load_step(ring[s], ent_cur, s, rows_left(nt0, s));
 
   for (int c = 0; c < nchunks; ++c) {
     const int c0 = t_begin + c * kChunkTokens;
     const int nt = min(kChunkTokens, t_end - c0);  // valid tokens of the chunk
-    // LDS bases rebuilt per chunk from an opaque zero, so constant per-step
-    // offsets fold into the instructions instead of each taking a register
-    const int z = opaque_zero();
-    // QK: head col, keys 4*quad..+3; lanes of padding heads write the junk row
-    // (a select, not a branch: divergent branches would split the step into
-    // blocks across which the compiler sinks the arithmetic, stretching the
-    // ring's live ranges)
-    float* s_wr = col < G ? sw + z + col * kWaveTokens + quad * 4
-                          : &s_junk[wave][0] + z + quad * 4;
-    float* sw_c = sw + z;
-    const uint32_t* p_rd = reinterpret_cast<const uint32_t*>(sw + z) + tg * NPAIR;
+    const int nt_next = min(kChunkTokens, t_end - c0 - kChunkTokens);
+    floatx4_t st[kWaveBlocks];  // raw scores: keys 4*quad+e of block i, head col
+    uint4 pa[kWaveBlocks / 2];  // bf16 probabilities: A operand of block pair j
 
     static_for<STEPS>([&](auto step_c) {
       constexpr int step = decltype(step_c)::value;
       uint32_t(&cur)[SLOT] = ring[step % DEPTH];
       constexpr int i = step & (kWaveBlocks - 1);
-      const int left = nt - (wave + kWaves * i) * kBlockSize;  // uniform: rows of block i in range
 
       if constexpr (step < kWaveBlocks) {
         // ---- QK on block i: S^T (16 keys x 16 heads) ---------------------------
-        floatx4_t st = {0.f, 0.f, 0.f, 0.f};
+        const int left = rows_left(nt, step);
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint4 t = make_uint4(cur[4 * ks], cur[4 * ks + 1], cur[4 * ks + 2], cur[4 * ks + 3]);
-          st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t), qb[ks], st,
-                                                       0, 0, 0);
-        }
-        float4 sv;
-        sv.x = quad * 4 + 0 < left ? st[0] * scale_log2 : -INFINITY;
-        sv.y = quad * 4 + 1 < left ? st[1] * scale_log2 : -INFINITY;
-        sv.z = quad * 4 + 2 < left ? st[2] * scale_log2 : -INFINITY;
-        sv.w = quad * 4 + 3 < left ? st[3] * scale_log2 : -INFINITY;
-        *reinterpret_cast<float4*>(s_wr + (col < G ? i * kBlockSize : 0)) = sv;
+        for (int ks = 0; ks < KS; ++ks)
+          acc = mfma_bf16(make_uint4(cur[4 * ks], cur[4 * ks + 1], cur[4 * ks + 2], cur[4 * ks + 3]),
+                          qb[ks], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[i][e] = 4 * quad + e < left ? acc[e] : -INFINITY;
+        // refill the slot just consumed
+        constexpr int ns = step + DEPTH;
+        if constexpr (ns < STEPS) load_step(cur, ent_cur, ns, rows_left(nt, ns));
+        else if constexpr (!ONE) load_step(cur, ent_nxt, ns - STEPS, rows_left(nt_next, ns - STEPS));
       } else {
         if constexpr (step == kWaveBlocks) {
-          // ---- P: online softmax over this wave's 128 rows --------------------------
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          // lane holds keys 2*lane, 2*lane+1 of the slice: block lane/8, pair lane%8
-          float2 sv[G];
+          // ---- P: online softmax over this wave's 8 blocks -------------------------
+          float mx = -INFINITY;
 #pragma unroll
-          for (int h = 0; h < G; ++h)
-            sv[h] = reinterpret_cast<const float2*>(sw_c + h * kWaveTokens)[lane];
-          const int pm = lane & 7;
-          const int p_idx = (lane >> 3) * kBlockSize + (pm % TG) * NPAIR + pm / TG;
+          for (int j = 0; j < kWaveBlocks; ++j)
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float m_new = uniform(fmaxf(m_run[h], wave_max(fmaxf(sv[h].x, sv[h].y))));
-            // a wave whose rows are all past the end keeps m = -inf; p = 0 then
-            const float ref = m_new == -INFINITY ? 0.f : m_new;
-            const uint32_t pk = pack_bf16x2(exp2f(sv[h].x - ref), exp2f(sv[h].y - ref));
-            // the normaliser sums the rounded probabilities the PV step applies
-            const float psum = bf16lo(pk) + bf16hi(pk);
-            reinterpret_cast<uint32_t*>(sw_c + h * kWaveTokens)[p_idx] = pk;
-            const float alpha = exp2f(m_run[h] - ref);
-            l_run[h] = uniform(l_run[h] * alpha + wave_sum(psum));
-            m_run[h] = m_new;
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, st[j][e]);
+          mx = fmaxf(mx, swap16(mx));
+          mx = fmaxf(mx, swap32(mx));
+          const float m_new = fmaxf(m_run, mx);
+          // no key of this head in range yet: m stays -inf and every p is 0
+          const float ref = m_new == -INFINITY ? 0.f : m_new * scale_log2;
+          const float alpha = fast_exp2(m_run * scale_log2 - ref);
+          m_run = m_new;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[h][e] *= alpha;
+          for (int j = 0; j < kWaveBlocks / 2; ++j) {
+            const floatx4_t& sa = st[2 * j];
+            const floatx4_t& sb = st[2 * j + 1];
+            pa[j].x = cvt_bf16x2(fast_exp2(fmaf(sa[0], scale_log2, -ref)), fast_exp2(fmaf(sa[1], scale_log2, -ref)));
+            pa[j].y = cvt_bf16x2(fast_exp2(fmaf(sa[2], scale_log2, -ref)), fast_exp2(fmaf(sa[3], scale_log2, -ref)));
+            pa[j].z = cvt_bf16x2(fast_exp2(fmaf(sb[0], scale_log2, -ref)), fast_exp2(fmaf(sb[1], scale_log2, -ref)));
+            pa[j].w = cvt_bf16x2(fast_exp2(fmaf(sb[2], scale_log2, -ref)), fast_exp2(fmaf(sb[3], scale_log2, -ref)));
           }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-        // ---- PV on block i ------------------------------------------------------
-        uint32_t(&vv)[SLOT] = cur;  // consumed in place; refilled after this step
+          // rescale the accumulators: lane (col, quad) holds heads 4*quad+e
+          float a[4];
 #pragma unroll
-        for (int k = 0; k < NPAIR; ++k)
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const bool in = 2 * (tg + TG * k) + e < left;  // selects, no branch
-            vv[4 * k + 2 * e] = in ? vv[4 * k + 2 * e] : 0u;
-            vv[4 * k + 2 * e + 1] = in ? vv[4 * k + 2 * e + 1] : 0u;
+          for (int e = 0; e < 4; ++e) {
+            const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), e));
+            const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 4 + e));
+            a[e] = quad == 0 ? lo : hi;
           }
-        uint32_t pp[G][NPAIR];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const uint32_t* src = p_rd + h * kWaveTokens + i * kBlockSize;
-          if constexpr (NPAIR == 4) {
-            const uint4 t = *reinterpret_cast<const uint4*>(src);
-            pp[h][0] = t.x; pp[h][1] = t.y; pp[h][2] = t.z; pp[h][3] = t.w;
-          } else {
-            const uint2 t = *reinterpret_cast<const uint2*>(src);
-            pp[h][0] = t.x; pp[h][1] = t.y;
+          for (int e = 0; e < 4; ++e) {
+            lacc[e] *= a[e];
+#pragma unroll
+            for (int s = 0; s < DPL; ++s) o[s][e] *= a[e];
           }
         }
+        if constexpr (i % 2 == 1) {
+          // ---- PV on blocks i-1, i: 32 keys ---------------------------------------
+          uint32_t(&va)[SLOT] = ring[(step - 1) % DEPTH];
+          uint32_t(&vb)[SLOT] = cur;
+          const uint4 pj = pa[i / 2];
 #pragma unroll
-        for (int k = 0; k < NPAIR; ++k) {
-          const uint32_t a0 = vv[4 * k], a1 = vv[4 * k + 1];      // row 2m: dims 0-1, 2-3
-          const uint32_t b0 = vv[4 * k + 2], b1 = vv[4 * k + 3];  // row 2m+1
-          const uint32_t d0 = interleave_lo(a0, b0), d1 = interleave_hi(a0, b0);
-          const uint32_t d2 = interleave_lo(a1, b1), d3 = interleave_hi(a1, b1);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            acc[h][0] = dot2_bf16(pp[h][k], d0, acc[h][0]);
-            acc[h][1] = dot2_bf16(pp[h][k], d1, acc[h][1]);
-            acc[h][2] = dot2_bf16(pp[h][k], d2, acc[h][2]);
-            acc[h][3] = dot2_bf16(pp[h][k], d3, acc[h][3]);
+          for (int s = 0; s < DPL; ++s) {
+            const int w = s / 2;
+            uint4 bv;
+            if (s % 2 == 0) {
+              bv.x = interleave_lo(va[w], va[HALF + w]);
+              bv.y = interleave_lo(va[2 * HALF + w], va[3 * HALF + w]);
+              bv.z = interleave_lo(vb[w], vb[HALF + w]);
+              bv.w = interleave_lo(vb[2 * HALF + w], vb[3 * HALF + w]);
+            } else {
+              bv.x = interleave_hi(va[w], va[HALF + w]);
+              bv.y = interleave_hi(va[2 * HALF + w], va[3 * HALF + w]);
+              bv.z = interleave_hi(vb[w], vb[HALF + w]);
+              bv.w = interleave_hi(vb[2 * HALF + w], vb[3 * HALF + w]);
+            }
+            o[s] = mfma_bf16(pj, bv, o[s]);
           }
-        }
-        if constexpr (step == STEPS - 1) {
-          // this chunk's probabilities consumed before the next chunk's QK overwrites them
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          lacc = mfma_bf16(pj, ones, lacc);
+          // refill both slots of the pair
+          constexpr int na = step - 1 + DEPTH, nb = step + DEPTH;
+          if constexpr (nb < STEPS) {
+            load_step(va, ent_cur, na, rows_left(nt, na));
+            load_step(vb, ent_cur, nb, rows_left(nt, nb));
+          } else if constexpr (!ONE) {
+            load_step(va, ent_nxt, na - STEPS, rows_left(nt_next, na - STEPS));
+            load_step(vb, ent_nxt, nb - STEPS, rows_left(nt_next, nb - STEPS));
+          }
         }
       }
-      // refill the slot just consumed: DEPTH steps ahead (into the next chunk near the end)
-      constexpr int ns = step + DEPTH;
-      if constexpr (ns < STEPS)
-        load_step(cur, ent_cur, ns);
-      else if constexpr (!ONE)
-        load_step(cur, ent_nxt, ns - STEPS);  // last chunk: ent_nxt re-reads its own blocks
-      // keep the refill here: hoisting later steps' loads would hold every
-      // block of the chunk in registers at once
+      // keep each step's loads here: hoisting later steps' loads would hold
+      // every block of the chunk in registers at once
       __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (!ONE) {
@@ -314,35 +302,20 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
     }
   }
 
-  // ---- combine row groups (lanes) and waves, write ----------------------------
+  // ---- combine the waves through LDS, write ------------------------------------
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int e = 0; e < 4; ++e)
+    if (4 * quad + e < G) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float x = acc[h][e];
-#pragma unroll
-      for (int off = VL; off < 64; off <<= 1) x += __shfl_xor(x, off);
-      acc[h][e] = x;
+      for (int s = 0; s < DPL; ++s) red[wave][4 * quad + e][s * 16 + col] = o[s][e];
+      if (col == 0) st_l[wave][4 * quad + e] = lacc[e];
     }
-  __syncthreads();  // every wave is done with its score slice
-  float* red = s_buf;  // [kWaves][G][D]
-  if (lane < VL) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      *reinterpret_cast<float4*>(red + (wave * G + h) * D + dq * 4) =
-          make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      st_m[wave][h] = m_run[h];
-      st_l[wave][h] = l_run[h];
-    }
-  }
+  if (quad == 0 && col < G) st_m[wave][col] = m_run * scale_log2;
   __syncthreads();
   for (int e = threadIdx.x; e < G * D / 4; e += blockDim.x) {
     const int h = e / (D / 4);
-    const int d4 = (e % (D / 4)) * 4;
+    const int d4 = (e % (D / 4)) * 4;  // dims d4..d4+3: lane n = d4 / DPL, tiles s0..s0+3
+    const int n = d4 / DPL, s0 = d4 % DPL;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, st_m[w][h]);
@@ -350,9 +323,9 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
     float lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float wt = st_m[w][h] == -INFINITY ? 0.f : exp2f(st_m[w][h] - M);
-      const float4 t = *reinterpret_cast<const float4*>(red + (w * G + h) * D + d4);
-      sum.x += wt * t.x; sum.y += wt * t.y; sum.z += wt * t.z; sum.w += wt * t.w;
+      const float wt = st_m[w][h] == -INFINITY ? 0.f : fast_exp2(st_m[w][h] - M);
+      const float* r = &red[w][h][s0 * 16 + n];
+      sum.x += wt * r[0]; sum.y += wt * r[16]; sum.z += wt * r[32]; sum.w += wt * r[48];
       lsum += wt * st_l[w][h];
     }
     const float inv = 1.f / lsum;
@@ -362,10 +335,10 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
           make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
       if (d4 == 0) lse[row * num_parts + p] = M + log2f(lsum);
     } else {
-      uint2 o;
-      o.x = pack_bf16x2(sum.x * inv, sum.y * inv);
-      o.y = pack_bf16x2(sum.z * inv, sum.w * inv);
-      *reinterpret_cast<uint2*>(out + row * D + d4) = o;
+      uint2 ov;
+      ov.x = pack_bf16x2(sum.x * inv, sum.y * inv);
+      ov.y = pack_bf16x2(sum.z * inv, sum.w * inv);
+      *reinterpret_cast<uint2*>(out + row * D + d4) = ov;
     }
   }
 }

@@ -47,6 +47,20 @@ __device__ __forceinline__ int opaque_zero() {
   return z;
 }
 
+// Loads of data read once per launch (K/V tiles), with the non-temporal hint:
+// the lines are not kept for reuse, which streams a gather of scattered 4 KiB
+// tiles faster than ordinary loads do.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_stream8(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(static_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+
 // Wave-uniform float into a scalar register.
 __device__ __forceinline__ float uniform(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
