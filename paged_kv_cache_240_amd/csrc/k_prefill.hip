@@ -9,22 +9,28 @@
 //
 // Rows are (position, head) pairs of one (sequence, KV head), position-major
 // (r = pos * G + h), so the G query heads sharing a KV head share every K/V
-// tile.  Workgroup = 4 waves over 128 rows; a wave owns 2 row tiles of 16.
-// Keys are walked in tiles of 32 (two 16-token blocks), double-buffered in
-// LDS, the next tile's global loads in flight while the current one computes.
+// tile.  Workgroup = 8 waves over 128 rows: the keys the rows can see are
+// split in two halves, and wave w takes row tiles 2(w%4), 2(w%4)+1 (16 rows
+// each) over half w/4.  Each half streams its keys in tiles of 32 (two
+// 16-token blocks) through a double-buffered LDS stage, filled from registers
+// loaded two tiles ahead.  Per tile and wave:
 //   QK   S^T (keys x rows) = K Q^T with v_mfma_f32_16x16x32_bf16: A = K tile
 //        from LDS (16-byte chunks XOR-swizzled by key so the 16 rows of an
 //        operand read hit distinct banks), B = the rows' queries (registers).
-//   P    online softmax per row (the row is a lane column: 8 scores per lane,
-//        max/sum across the 4 lanes sharing it by row swaps); rows' causal
-//        limits are applied by selects on tiles crossing the diagonal.  p is
-//        rounded to bf16; the S^T accumulator layout is already the B operand
-//        of the PV product, so p never moves.
-//   PV   O^T (dims x rows) += V^T P^T: A = V^T from LDS, where V is stored
-//        transposed with the key order the P operand implies (8 keys of a
-//        lane contiguous) and an 80-byte row stride (conflict-free reads).
-// Keys at or past L are written to LDS as zeros (never multiplied by 0: NaN
-// in unused slots cannot leak) and their table entries are never read.
+//   P    per row (a lane column: 8 scores per lane, 4 lanes per row) the
+//        running reference max is raised only when a tile's max exceeds it by
+//        more than 2^8 (p then stays below 256: exact enough in bf16, safe in
+//        fp32 sums), which spares nearly every rescale of the accumulators.
+//        Causal limits are applied by selects on tiles crossing the diagonal.
+//        p is rounded to bf16; the S^T accumulator layout is already the B
+//        operand of the PV product, so p never moves.
+//   PV   O^T (dims x rows) += V^T P^T: A = V^T from LDS, V stored transposed
+//        with the key order the P operand implies (8 keys of a lane
+//        contiguous) and an 80-byte row stride (conflict-free reads); a
+//        ninth product against a ones operand accumulates the normaliser.
+// The two halves meet through LDS at the end (log-sum-exp merge).  Keys at or
+// past L are written to LDS as zeros (never multiplied by 0: NaN in unused
+// slots cannot leak) and their table entries are never read.
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -35,12 +41,16 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
-constexpr int kRowTiles = 2;                    // 16-row tiles per wave
-constexpr int kRowsPerWave = 16 * kRowTiles;    // 32
-constexpr int kRowsPerWG = kWaves * kRowsPerWave;  // 128
-constexpr int kKeyTile = 32;                    // keys per step (two blocks)
-constexpr int kVtStride = 40;                   // bf16 per V^T row: 32 keys + 8 pad (80 bytes)
+constexpr int kHalves = 2;                       // key ranges per workgroup
+constexpr int kWavesPerHalf = 4;
+constexpr int kThreads = 64 * kHalves * kWavesPerHalf;  // 512
+constexpr int kHalfThreads = 64 * kWavesPerHalf;        // 256: one half's stream
+constexpr int kRowTiles = 2;                     // 16-row tiles per wave
+constexpr int kRowsPerWave = 16 * kRowTiles;     // 32
+constexpr int kRowsPerWG = kWavesPerHalf * kRowsPerWave;  // 128
+constexpr int kKeyTile = 32;                     // keys per step (two blocks)
+constexpr int kVtStride = 40;                    // bf16 per V^T row: 32 keys + 8 pad (80 bytes)
+constexpr float kLazyLog2 = 8.f;                 // reference max may lag the true one by 2^8
 
 // LDS position of key k (0..31) in a V^T row: lane group q reads its 8 keys
 // 4q..4q+3 and 16+4q..16+4q+3 (the keys its S^T registers hold) contiguously.
@@ -48,8 +58,17 @@ __device__ __forceinline__ int vt_pos(int k) {
   return k < 16 ? 8 * (k >> 2) + (k & 3) : 8 * ((k - 16) >> 2) + 4 + (k & 3);
 }
 
+__device__ __forceinline__ floatx4_t mfma_bf16(bf16x8_t a, bf16x8_t b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  const bf16x2_t r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 template <int D, int G>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kThreads)
 prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
                const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
@@ -58,17 +77,23 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   constexpr int NCH = D / 8;         // 16-byte chunks per row
   constexpr int KS = D / 32;         // MFMA k-steps over the head dimension
   constexpr int DT = D / 16;         // 16-dim output tiles
-  constexpr int TILE_CHUNKS = 2 * kBlockSize * NCH;  // 16-byte chunks of a K (or V) tile
-  constexpr int LOADS = TILE_CHUNKS / 256;           // per thread, per operand
-  static_assert(TILE_CHUNKS % 256 == 0, "tile chunks must spread evenly over the workgroup");
+  constexpr int K_LOADS = 2 * kBlockSize * NCH / kHalfThreads;  // K chunks per thread per tile
+  static_assert(K_LOADS >= 1 && (2 * kBlockSize * NCH) % kHalfThreads == 0, "K tile split");
+  constexpr int V_UNITS = (kKeyTile / 2) * NCH;  // (key pair, 8-dim chunk) units of a V tile
+  static_assert(V_UNITS <= kHalfThreads, "one V unit per thread at most");
   constexpr int KS_BYTES = kKeyTile * D * 2;
   constexpr int VT_BYTES = D * kVtStride * 2;
+  constexpr int BUF_BYTES = KS_BYTES + VT_BYTES;
+  constexpr int MERGE_FLOATS = kWavesPerHalf * kRowTiles * (DT * 4 + 2) * 64;
+  static_assert(MERGE_FLOATS * 4 <= kHalves * 2 * BUF_BYTES, "merge area fits the tile buffers");
 
-  __shared__ __align__(16) unsigned char lds[2][KS_BYTES + VT_BYTES];
+  __shared__ __align__(16) unsigned char lds[kHalves][2][BUF_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave / kWavesPerHalf, hw = wave % kWavesPerHalf;
+  const int htid = tid % kHalfThreads;
   const int col = lane & 15, quad = lane >> 4;
   const int rb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int Hq = Hkv * G;
@@ -83,6 +108,9 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   // keys any row of this workgroup can see: up to position L - C + pos_max
   const int kmax = min(L, L - C + pos_last / G + 1);
   const int ntiles = (kmax + kKeyTile - 1) / kKeyTile;
+  const int nsteps = (ntiles + 1) / 2;                 // tiles of half 0 (half 1 has <= as many)
+  const int tile0 = half * nsteps;                     // first tile of this wave's half
+  const int tile_end = half == 0 ? nsteps : ntiles;    // one past its last tile
   const int nblk_seq = (L + kBlockSize - 1) / kBlockSize;
   const int32_t* bt_row = block_tables + (int64_t)b * max_blocks;
   const int64_t head_off = (int64_t)g * kBlockSize * D;
@@ -94,7 +122,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   bf16x8_t qb[kRowTiles][KS];
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt) {
-    const int r = row0_wg + wave * kRowsPerWave + rt * 16 + col;
+    const int r = row0_wg + hw * kRowsPerWave + rt * 16 + col;
     rvalid[rt] = r < nrows;
     const int pos = rvalid[rt] ? r / G : 0;
     const int h = rvalid[rt] ? r % G : 0;
@@ -107,83 +135,90 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
       qb[rt][ks] = __builtin_bit_cast(bf16x8_t, t);
     }
   }
-  int lim_min = lim[0];
-#pragma unroll
-  for (int rt = 1; rt < kRowTiles; ++rt) lim_min = min(lim_min, lim[rt]);
   // smallest causal limit over the workgroup's rows (tiles past it need masks)
   const int lim_min_wg = L - C + row0_wg / G;
 
-  // ---- staging: global -> registers -> LDS ------------------------------------
-  uint4 kreg[LOADS], vreg[LOADS];
-  auto load_tile = [&](int tt) {
+  // ---- staging: global -> registers (two tiles ahead) -> LDS ----------------------
+  struct Stage { uint4 k[K_LOADS]; uint4 v0, v1; };
+  // tile tt of this half; tiles past the half's range load nothing
+  auto load_tile = [&](Stage& st, int tt) {
+    const bool live = tt < tile_end;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      // K: chunk c covers block c / (16 NCH), key row, 16-byte chunk (coalesced rows)
-      const int c = tid + 256 * i;
+    for (int i = 0; i < K_LOADS; ++i) {
+      // chunk c: block c / (16 NCH), key row, 16-byte chunk (coalesced rows)
+      const int c = htid + kHalfThreads * i;
       const int blk = c / (kBlockSize * NCH);
       const int key = (c / NCH) % kBlockSize;
       const int ch = c % NCH;
       const int lb = tt * 2 + blk;
       const int t = lb * kBlockSize + key;
       uint4 kv = make_uint4(0u, 0u, 0u, 0u);
-      if (lb < nblk_seq && t < L)
+      if (live && lb < nblk_seq && t < L)
         kv = *reinterpret_cast<const uint4*>(k_cache + (int64_t)bt_row[lb] * blk_stride +
                                              head_off + key * D + ch * 8);
-      kreg[i] = kv;
-      // V: chunk c covers key c % 32 and dims 8*(c / 32) .. +7
-      const int vkey = c % kKeyTile;
-      const int vch = c / kKeyTile;
-      const int vlb = tt * 2 + vkey / kBlockSize;
-      const int vt = vlb * kBlockSize + vkey % kBlockSize;
-      uint4 vv = make_uint4(0u, 0u, 0u, 0u);
-      if (vlb < nblk_seq && vt < L)
-        vv = *reinterpret_cast<const uint4*>(v_cache + (int64_t)bt_row[vlb] * blk_stride +
-                                             head_off + (vkey % kBlockSize) * D + vch * 8);
-      vreg[i] = vv;
+      st.k[i] = kv;
     }
+    // V unit u: keys 2(u % 16), 2(u % 16)+1 of the tile, dims 8(u / 16) .. +7
+    const int u = htid;
+    const int k0 = 2 * (u % (kKeyTile / 2));
+    const int vch = u / (kKeyTile / 2);
+    const int lb = tt * 2 + k0 / kBlockSize;
+    const int t = lb * kBlockSize + k0 % kBlockSize;
+    uint4 a = make_uint4(0u, 0u, 0u, 0u), c = make_uint4(0u, 0u, 0u, 0u);
+    if (live && u < V_UNITS && lb < nblk_seq) {
+      const uint16_t* src = v_cache + (int64_t)bt_row[lb] * blk_stride + head_off +
+                            (k0 % kBlockSize) * D + vch * 8;
+      if (t < L) a = *reinterpret_cast<const uint4*>(src);
+      if (t + 1 < L) c = *reinterpret_cast<const uint4*>(src + D);
+    }
+    st.v0 = a;
+    st.v1 = c;
   };
-  auto store_tile = [&](int buf) {
-    unsigned char* ks_base = lds[buf];
-    uint16_t* vt_base = reinterpret_cast<uint16_t*>(lds[buf] + KS_BYTES);
+  auto store_tile = [&](const Stage& st, int buf) {
+    unsigned char* ks_base = lds[half][buf];
+    uint16_t* vt_base = reinterpret_cast<uint16_t*>(lds[half][buf] + KS_BYTES);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i;
+    for (int i = 0; i < K_LOADS; ++i) {
+      const int c = htid + kHalfThreads * i;
       const int key = (c / NCH) % kBlockSize + kBlockSize * (c / (kBlockSize * NCH));
       const int ch = c % NCH;
-      *reinterpret_cast<uint4*>(ks_base + key * D * 2 + ((ch ^ (key & (NCH - 1))) * 16)) = kreg[i];
-      const int vkey = c % kKeyTile;
-      const int d0 = 8 * (c / kKeyTile);
-      uint16_t* dst = vt_base + d0 * kVtStride + vt_pos(vkey);
-      const uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+      *reinterpret_cast<uint4*>(ks_base + key * D * 2 + ((ch ^ (key & (NCH - 1))) * 16)) = st.k[i];
+    }
+    const int u = htid;
+    if (u < V_UNITS) {
+      const int k0 = 2 * (u % (kKeyTile / 2));
+      const int d0 = 8 * (u / (kKeyTile / 2));
+      uint32_t* dst = reinterpret_cast<uint32_t*>(vt_base + d0 * kVtStride + vt_pos(k0));
+      const uint32_t a[4] = {st.v0.x, st.v0.y, st.v0.z, st.v0.w};
+      const uint32_t c[4] = {st.v1.x, st.v1.y, st.v1.z, st.v1.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        dst[(2 * e) * kVtStride] = (uint16_t)(w[e] & 0xFFFFu);
-        dst[(2 * e + 1) * kVtStride] = (uint16_t)(w[e] >> 16);
+        // dims 2e, 2e+1 of the chunk: (key k0, key k0+1) pairs
+        dst[(2 * e) * kVtStride / 2] = interleave_lo(a[e], c[e]);
+        dst[(2 * e + 1) * kVtStride / 2] = interleave_hi(a[e], c[e]);
       }
     }
   };
 
   floatx4_t o[DT][kRowTiles];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) o[dt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[kRowTiles], l_part[kRowTiles];
+  floatx4_t lacc[kRowTiles];
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt) {
-    m_run[rt] = -INFINITY;
-    l_part[rt] = 0.f;
+    lacc[rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
+  float m_ref[kRowTiles];  // reference max of the row (raw scores; -inf: none seen)
+#pragma unroll
+  for (int rt = 0; rt < kRowTiles; ++rt) m_ref[rt] = -INFINITY;
+  const float lazy_raw = kLazyLog2 / scale_log2;
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
+                                                                0x3F803F80u, 0x3F803F80u));
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const int buf = tt & 1;
-    if (tt + 1 < ntiles) load_tile(tt + 1);
-    const unsigned char* ks_base = lds[buf];
-    const uint16_t* vt_base = reinterpret_cast<const uint16_t*>(lds[buf] + KS_BYTES);
+  // one tile of this half from LDS buffer `buf`
+  auto compute_tile = [&](int tt, int buf) {
+    const unsigned char* ks_base = lds[half][buf];
+    const uint16_t* vt_base = reinterpret_cast<const uint16_t*>(lds[half][buf] + KS_BYTES);
     const int key0 = tt * kKeyTile;
 
     // ---- QK: S^T for 2 key tiles x 2 row tiles ----------------------------------
@@ -200,12 +235,11 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                                                         ((ch ^ (key & (NCH - 1))) * 16));
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
 #pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt)
-          st[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[rt][ks], st[kt][rt], 0, 0, 0);
+        for (int rt = 0; rt < kRowTiles; ++rt) st[kt][rt] = mfma_bf16(av, qb[rt][ks], st[kt][rt]);
       }
     }
 
-    // ---- P: online softmax per row ----------------------------------------------
+    // ---- P: softmax numerators against a lazily raised reference max ------------
     const bool need_mask = key0 + kKeyTile - 1 > lim_min_wg;
     bf16x8_t pb[kRowTiles];
 #pragma unroll
@@ -215,30 +249,30 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float x = st[kt][rt][j] * scale_log2;
           const int t = key0 + kt * 16 + quad * 4 + j;
-          s[kt * 4 + j] = (!need_mask || t <= lim[rt]) ? x : -INFINITY;
+          s[kt * 4 + j] = (!need_mask || t <= lim[rt]) ? st[kt][rt][j] : -INFINITY;
         }
-      float mt = s[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, s[e]);
+      float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                       fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
       mt = fmaxf(mt, swap16(mt));
       mt = fmaxf(mt, swap32(mt));
-      const float m_new = fmaxf(m_run[rt], mt);
-      const float ref = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run[rt] - ref);
-      m_run[rt] = m_new;
-      uint32_t pk[4];
-      float ps = 0.f;
+      const bool raise = mt > m_ref[rt] + lazy_raw;  // false for -inf tiles
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        // rows that keep their reference scale by exactly 1 (their m_ref may be -inf)
+        const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref[rt] - mt) * scale_log2) : 1.f;
+        m_ref[rt] = raise ? mt : m_ref[rt];
+        lacc[rt] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pk[e] = pack_bf16x2(exp2f(s[2 * e] - ref), exp2f(s[2 * e + 1] - ref));
-        ps += bf16lo(pk[e]) + bf16hi(pk[e]);  // the normaliser sums what PV applies
+        for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
       }
-      l_part[rt] = l_part[rt] * alpha + ps;
-      pb[rt] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+      const float refc = m_ref[rt] == -INFINITY ? 0.f : m_ref[rt] * scale_log2;
+      uint32_t pk[4];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
+      for (int e = 0; e < 4; ++e)
+        pk[e] = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[2 * e], scale_log2, -refc)),
+                           __builtin_amdgcn_exp2f(fmaf(s[2 * e + 1], scale_log2, -refc)));
+      pb[rt] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+      lacc[rt] = mfma_bf16(ones, pb[rt], lacc[rt]);
     }
 
     // ---- PV: O^T += V^T P^T ---------------------------------------------------------
@@ -247,32 +281,70 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
       const uint4 a = *reinterpret_cast<const uint4*>(vt_base + (dt * 16 + col) * kVtStride + quad * 8);
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
 #pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt)
-        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[rt], o[dt][rt], 0, 0, 0);
+      for (int rt = 0; rt < kRowTiles; ++rt) o[dt][rt] = mfma_bf16(av, pb[rt], o[dt][rt]);
     }
+  };
 
-    if (tt + 1 < ntiles) store_tile(buf ^ 1);
+  // ---- main loop: both halves in step; tiles past a half's range are skipped ---------
+  Stage sa, sb;
+  load_tile(sa, tile0);
+  load_tile(sb, tile0 + 1);
+  store_tile(sa, 0);
+  __syncthreads();
+  for (int i = 0; i < nsteps; i += 2) {
+    // even step: tile tile0+i in buffer 0, tile+1 staged in sb, tile+2 loads into sa
+    load_tile(sa, tile0 + i + 2);
+    if (tile0 + i < tile_end) compute_tile(tile0 + i, 0);
+    store_tile(sb, 1);
+    __syncthreads();
+    if (i + 1 >= nsteps) break;
+    // odd step: tile tile0+i+1 in buffer 1, tile+1 staged in sa, tile+2 loads into sb
+    load_tile(sb, tile0 + i + 3);
+    if (tile0 + i + 1 < tile_end) compute_tile(tile0 + i + 1, 1);
+    store_tile(sa, 0);
     __syncthreads();
   }
 
-  // ---- normalise and write: lane holds O^T[dims 4*quad+j of tile dt][row col] ---------
+  // ---- merge the halves through LDS, normalise and write ------------------------------
+  // lane holds O^T[dims 4*quad+j of tile dt][row col]; l of row col in lacc[rt][0]
+  float* mg = reinterpret_cast<float*>(&lds[0][0][0]);  // [hw][rt][DT*4 + 2][64]
+  auto mg_at = [&](int rt, int k) -> float& {
+    return mg[((hw * kRowTiles + rt) * (DT * 4 + 2) + k) * 64 + lane];
+  };
+  if (half == 1) {
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mg_at(rt, dt * 4 + j) = o[dt][rt][j];
+      mg_at(rt, DT * 4) = m_ref[rt];
+      mg_at(rt, DT * 4 + 1) = lacc[rt][0];
+    }
+  }
+  __syncthreads();
+  if (half == 1) return;
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt) {
-    float l = l_part[rt];
-    l += swap16(l);
-    l += swap32(l);
+    const float m1 = mg_at(rt, DT * 4), l1 = mg_at(rt, DT * 4 + 1);
+    const float m0 = m_ref[rt], l0 = lacc[rt][0];
+    const float M = fmaxf(m0, m1);
+    const float w0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m0 - M) * scale_log2);
+    const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - M) * scale_log2);
+    const float inv = 1.f / (w0 * l0 + w1 * l1);
     if (!rvalid[rt]) continue;
-    const float inv = 1.f / l;
-    const int r = row0_wg + wave * kRowsPerWave + rt * 16 + col;
+    const int r = row0_wg + hw * kRowsPerWave + rt * 16 + col;
     const int pos = r / G, h = r % G;
     uint16_t* orow = out + ((int64_t)(q0 + pos) * Hq + g * G + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt) {
+      float y[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = (w0 * o[dt][rt][j] + w1 * mg_at(rt, dt * 4 + j)) * inv;
       *reinterpret_cast<uint2*>(orow + dt * 16 + quad * 4) =
-          make_uint2(pack_bf16x2(o[dt][rt][0] * inv, o[dt][rt][1] * inv),
-                     pack_bf16x2(o[dt][rt][2] * inv, o[dt][rt][3] * inv));
+          make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+    }
   }
-  (void)lim_min;
 }
 
 template <int D>
@@ -280,7 +352,7 @@ hipError_t launch_d(int G, dim3 grid, hipStream_t stream, uint16_t* out, const u
                     const uint16_t* kc, const uint16_t* vc, const int32_t* bt, const int32_t* cl,
                     const int32_t* qsl, int Hkv, int mb, float sl) {
 #define PA_PREFILL(GG)                                                                        \
-  hipLaunchKernelGGL((prefill_kernel<D, GG>), grid, dim3(256), 0, stream, out, q, kc, vc, bt,  \
+  hipLaunchKernelGGL((prefill_kernel<D, GG>), grid, dim3(kThreads), 0, stream, out, q, kc, vc, bt,  \
                      cl, qsl, Hkv, mb, sl)
   switch (G) {
     case 1: PA_PREFILL(1); break;
