@@ -48,14 +48,18 @@ constexpr int kHalfThreads = 64 * kWavesPerHalf;        // 256: one half's strea
 constexpr int kRowTiles = 2;                     // 16-row tiles per wave
 constexpr int kRowsPerWave = 16 * kRowTiles;     // 32
 constexpr int kRowsPerWG = kWavesPerHalf * kRowsPerWave;  // 128
-constexpr int kKeyTile = 32;                     // keys per step (two blocks)
-constexpr int kVtStride = 40;                    // bf16 per V^T row: 32 keys + 8 pad (80 bytes)
+constexpr int kStepBlocks = 4;                   // 16-token blocks per step
+constexpr int kStepKeys = kStepBlocks * kBlockSize;  // 64
+constexpr int kPairs = kStepBlocks / 2;          // 32-key PV products per step
+constexpr int kVtStride = kStepKeys + 8;         // bf16 per V^T row: 64 keys + 8 pad (144 bytes)
 constexpr float kLazyLog2 = 8.f;                 // reference max may lag the true one by 2^8
 
-// LDS position of key k (0..31) in a V^T row: lane group q reads its 8 keys
-// 4q..4q+3 and 16+4q..16+4q+3 (the keys its S^T registers hold) contiguously.
+// LDS position of key k (0..63) in a V^T row: per 32-key pair, lane group q
+// reads its 8 keys 4q..4q+3 and 16+4q..16+4q+3 (the keys its S^T registers
+// hold) contiguously.
 __device__ __forceinline__ int vt_pos(int k) {
-  return k < 16 ? 8 * (k >> 2) + (k & 3) : 8 * ((k - 16) >> 2) + 4 + (k & 3);
+  const int kk = k & 31;
+  return (k & 32) + (kk < 16 ? 8 * (kk >> 2) + (kk & 3) : 8 * ((kk - 16) >> 2) + 4 + (kk & 3));
 }
 
 __device__ __forceinline__ floatx4_t mfma_bf16(bf16x8_t a, bf16x8_t b, floatx4_t c) {
@@ -77,11 +81,11 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   constexpr int NCH = D / 8;         // 16-byte chunks per row
   constexpr int KS = D / 32;         // MFMA k-steps over the head dimension
   constexpr int DT = D / 16;         // 16-dim output tiles
-  constexpr int K_LOADS = 2 * kBlockSize * NCH / kHalfThreads;  // K chunks per thread per tile
-  static_assert(K_LOADS >= 1 && (2 * kBlockSize * NCH) % kHalfThreads == 0, "K tile split");
-  constexpr int V_UNITS = (kKeyTile / 2) * NCH;  // (key pair, 8-dim chunk) units of a V tile
-  static_assert(V_UNITS <= kHalfThreads, "one V unit per thread at most");
-  constexpr int KS_BYTES = kKeyTile * D * 2;
+  constexpr int K_LOADS = kStepKeys * NCH / kHalfThreads;        // K chunks per thread per step
+  constexpr int V_LOADS = (kStepKeys / 2) * NCH / kHalfThreads;  // (key pair, 8-dim) V units
+  static_assert(K_LOADS >= 1 && V_LOADS >= 1 && (kStepKeys / 2) * NCH % kHalfThreads == 0,
+                "tile loads spread evenly over a half's threads");
+  constexpr int KS_BYTES = kStepKeys * D * 2;
   constexpr int VT_BYTES = D * kVtStride * 2;
   constexpr int BUF_BYTES = KS_BYTES + VT_BYTES;
   constexpr int MERGE_FLOATS = kWavesPerHalf * kRowTiles * (DT * 4 + 2) * 64;
@@ -107,7 +111,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   const int pos_last = min(nrows, row0_wg + kRowsPerWG) - 1;  // last valid row of the WG
   // keys any row of this workgroup can see: up to position L - C + pos_max
   const int kmax = min(L, L - C + pos_last / G + 1);
-  const int ntiles = (kmax + kKeyTile - 1) / kKeyTile;
+  const int ntiles = (kmax + kStepKeys - 1) / kStepKeys;
   const int nsteps = (ntiles + 1) / 2;                 // tiles of half 0 (half 1 has <= as many)
   const int tile0 = half * nsteps;                     // first tile of this wave's half
   const int tile_end = half == 0 ? nsteps : ntiles;    // one past its last tile
@@ -138,41 +142,52 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   // smallest causal limit over the workgroup's rows (tiles past it need masks)
   const int lim_min_wg = L - C + row0_wg / G;
 
-  // ---- staging: global -> registers (two tiles ahead) -> LDS ----------------------
-  struct Stage { uint4 k[K_LOADS]; uint4 v0, v1; };
-  // tile tt of this half; tiles past the half's range load nothing
-  auto load_tile = [&](Stage& st, int tt) {
-    const bool live = tt < tile_end;
+  // ---- staging: global -> registers -> LDS ----------------------------------------
+  // A step is kStepBlocks blocks.  Every load is unconditional, from an
+  // address that is always valid, so no branch splits the load stream:
+  //  * table entries are clamped into the sequence's blocks; they are
+  //    wave-uniform scalar loads (a per-lane entry load would make the data
+  //    loads behind it wait for every load in flight);
+  //  * K rows at or past L are loaded but never seen: their scores are
+  //    replaced by -inf;
+  //  * V rows at or past L are redirected to the first row of the step (a
+  //    key below L), so NaN in unused slots cannot meet a zero probability.
+  // Steps past the half's range are loaded the same way and never computed.
+  struct Stage { u32x4_t k[K_LOADS]; u32x4_t v0[V_LOADS], v1[V_LOADS]; };  // native vectors: no memcpy, no stack
+  auto load_tile = [&](int tt) -> Stage {
+    Stage st;
+    const int lb0 = tt * kStepBlocks;
+    static_assert(kStepBlocks == 4, "four table entries per step");
+    const int ent0 = bt_row[min(lb0, nblk_seq - 1)];
+    const int ent1 = bt_row[min(lb0 + 1, nblk_seq - 1)];
+    const int ent2 = bt_row[min(lb0 + 2, nblk_seq - 1)];
+    const int ent3 = bt_row[min(lb0 + 3, nblk_seq - 1)];
 #pragma unroll
     for (int i = 0; i < K_LOADS; ++i) {
       // chunk c: block c / (16 NCH), key row, 16-byte chunk (coalesced rows)
       const int c = htid + kHalfThreads * i;
-      const int blk = c / (kBlockSize * NCH);
       const int key = (c / NCH) % kBlockSize;
       const int ch = c % NCH;
-      const int lb = tt * 2 + blk;
-      const int t = lb * kBlockSize + key;
-      uint4 kv = make_uint4(0u, 0u, 0u, 0u);
-      if (live && lb < nblk_seq && t < L)
-        kv = *reinterpret_cast<const uint4*>(k_cache + (int64_t)bt_row[lb] * blk_stride +
-                                             head_off + key * D + ch * 8);
-      st.k[i] = kv;
+      const int blk = c / (kBlockSize * NCH);
+      const int e = blk == 0 ? ent0 : blk == 1 ? ent1 : blk == 2 ? ent2 : ent3;
+      st.k[i] = *reinterpret_cast<const u32x4_t*>(k_cache + (int64_t)e * blk_stride + head_off +
+                                                  key * D + ch * 8);
     }
-    // V unit u: keys 2(u % 16), 2(u % 16)+1 of the tile, dims 8(u / 16) .. +7
-    const int u = htid;
-    const int k0 = 2 * (u % (kKeyTile / 2));
-    const int vch = u / (kKeyTile / 2);
-    const int lb = tt * 2 + k0 / kBlockSize;
-    const int t = lb * kBlockSize + k0 % kBlockSize;
-    uint4 a = make_uint4(0u, 0u, 0u, 0u), c = make_uint4(0u, 0u, 0u, 0u);
-    if (live && u < V_UNITS && lb < nblk_seq) {
-      const uint16_t* src = v_cache + (int64_t)bt_row[lb] * blk_stride + head_off +
-                            (k0 % kBlockSize) * D + vch * 8;
-      if (t < L) a = *reinterpret_cast<const uint4*>(src);
-      if (t + 1 < L) c = *reinterpret_cast<const uint4*>(src + D);
+#pragma unroll
+    for (int j = 0; j < V_LOADS; ++j) {
+      // V unit u: keys 2(u % 32), 2(u % 32)+1 of the step, dims 8(u / 32) .. +7
+      const int u = htid + kHalfThreads * j;
+      const int k0 = 2 * (u % (kStepKeys / 2));
+      const int t = lb0 * kBlockSize + k0;
+      const int vb = k0 / kBlockSize;
+      const int e = vb == 0 ? ent0 : vb == 1 ? ent1 : vb == 2 ? ent2 : ent3;
+      const int e_a = t < L ? e : ent0, r_a = t < L ? k0 % kBlockSize : 0;
+      const int e_b = t + 1 < L ? e : ent0, r_b = t + 1 < L ? k0 % kBlockSize + 1 : 0;
+      const uint16_t* vsrc = v_cache + head_off + (u / (kStepKeys / 2)) * 8;
+      st.v0[j] = *reinterpret_cast<const u32x4_t*>(vsrc + (int64_t)e_a * blk_stride + r_a * D);
+      st.v1[j] = *reinterpret_cast<const u32x4_t*>(vsrc + (int64_t)e_b * blk_stride + r_b * D);
     }
-    st.v0 = a;
-    st.v1 = c;
+    return st;
   };
   auto store_tile = [&](const Stage& st, int buf) {
     unsigned char* ks_base = lds[half][buf];
@@ -182,15 +197,16 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
       const int c = htid + kHalfThreads * i;
       const int key = (c / NCH) % kBlockSize + kBlockSize * (c / (kBlockSize * NCH));
       const int ch = c % NCH;
-      *reinterpret_cast<uint4*>(ks_base + key * D * 2 + ((ch ^ (key & (NCH - 1))) * 16)) = st.k[i];
+      *reinterpret_cast<u32x4_t*>(ks_base + key * D * 2 + ((ch ^ (key & (NCH - 1))) * 16)) = st.k[i];
     }
-    const int u = htid;
-    if (u < V_UNITS) {
-      const int k0 = 2 * (u % (kKeyTile / 2));
-      const int d0 = 8 * (u / (kKeyTile / 2));
+#pragma unroll
+    for (int j = 0; j < V_LOADS; ++j) {
+      const int u = htid + kHalfThreads * j;
+      const int k0 = 2 * (u % (kStepKeys / 2));
+      const int d0 = 8 * (u / (kStepKeys / 2));
       uint32_t* dst = reinterpret_cast<uint32_t*>(vt_base + d0 * kVtStride + vt_pos(k0));
-      const uint32_t a[4] = {st.v0.x, st.v0.y, st.v0.z, st.v0.w};
-      const uint32_t c[4] = {st.v1.x, st.v1.y, st.v1.z, st.v1.w};
+      const uint32_t a[4] = {st.v0[j].x, st.v0[j].y, st.v0[j].z, st.v0[j].w};
+      const uint32_t c[4] = {st.v1[j].x, st.v1[j].y, st.v1[j].z, st.v1[j].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // dims 2e, 2e+1 of the chunk: (key k0, key k0+1) pairs
@@ -215,48 +231,53 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
                                                                 0x3F803F80u, 0x3F803F80u));
 
-  // one tile of this half from LDS buffer `buf`
+  // one step of this half from LDS buffer `buf`
   auto compute_tile = [&](int tt, int buf) {
     const unsigned char* ks_base = lds[half][buf];
     const uint16_t* vt_base = reinterpret_cast<const uint16_t*>(lds[half][buf] + KS_BYTES);
-    const int key0 = tt * kKeyTile;
+    const int key0 = tt * kStepKeys;
 
-    // ---- QK: S^T for 2 key tiles x 2 row tiles ----------------------------------
-    floatx4_t st[2][kRowTiles];
+    // ---- QK: S^T for kStepBlocks key tiles x 2 row tiles -------------------------
+    floatx4_t st[kStepBlocks][kRowTiles];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) st[kt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < kStepBlocks; ++kt) {
       const int key = kt * 16 + col;
+      bf16x8_t ka[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int ch = ks * 4 + quad;
-        const uint4 a = *reinterpret_cast<const uint4*>(ks_base + key * D * 2 +
-                                                        ((ch ^ (key & (NCH - 1))) * 16));
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
-#pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) st[kt][rt] = mfma_bf16(av, qb[rt][ks], st[kt][rt]);
+        ka[ks] = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(ks_base + key * D * 2 + ((ch ^ (key & (NCH - 1))) * 16)));
       }
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt) {
+        st[kt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) st[kt][rt] = mfma_bf16(ka[ks], qb[rt][ks], st[kt][rt]);
+      }
+    }
+    // causal limits: only steps crossing some row's diagonal need the selects
+    if (key0 + kStepKeys - 1 > lim_min_wg) {
+#pragma unroll
+      for (int kt = 0; kt < kStepBlocks; ++kt)
+#pragma unroll
+        for (int rt = 0; rt < kRowTiles; ++rt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            st[kt][rt][j] = key0 + kt * 16 + quad * 4 + j <= lim[rt] ? st[kt][rt][j] : -INFINITY;
     }
 
     // ---- P: softmax numerators against a lazily raised reference max ------------
-    const bool need_mask = key0 + kKeyTile - 1 > lim_min_wg;
-    bf16x8_t pb[kRowTiles];
+    bf16x8_t pb[kPairs][kRowTiles];
 #pragma unroll
     for (int rt = 0; rt < kRowTiles; ++rt) {
-      float s[8];
+      float mt = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = key0 + kt * 16 + quad * 4 + j;
-          s[kt * 4 + j] = (!need_mask || t <= lim[rt]) ? st[kt][rt][j] : -INFINITY;
-        }
-      float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                       fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      for (int kt = 0; kt < kStepBlocks; ++kt)
+        mt = fmaxf(mt, fmaxf(fmaxf(st[kt][rt][0], st[kt][rt][1]), fmaxf(st[kt][rt][2], st[kt][rt][3])));
       mt = fmaxf(mt, swap16(mt));
       mt = fmaxf(mt, swap32(mt));
-      const bool raise = mt > m_ref[rt] + lazy_raw;  // false for -inf tiles
+      const bool raise = mt > m_ref[rt] + lazy_raw;  // false for -inf steps
       if (__builtin_amdgcn_ballot_w64(raise)) {
         // rows that keep their reference scale by exactly 1 (their m_ref may be -inf)
         const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref[rt] - mt) * scale_log2) : 1.f;
@@ -266,42 +287,45 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
       }
       const float refc = m_ref[rt] == -INFINITY ? 0.f : m_ref[rt] * scale_log2;
-      uint32_t pk[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pk[e] = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[2 * e], scale_log2, -refc)),
-                           __builtin_amdgcn_exp2f(fmaf(s[2 * e + 1], scale_log2, -refc)));
-      pb[rt] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-      lacc[rt] = mfma_bf16(ones, pb[rt], lacc[rt]);
+      for (int pp = 0; pp < kPairs; ++pp) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const floatx4_t& sv = st[2 * pp + h][rt];
+          pk[2 * h] = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[0], scale_log2, -refc)),
+                                 __builtin_amdgcn_exp2f(fmaf(sv[1], scale_log2, -refc)));
+          pk[2 * h + 1] = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[2], scale_log2, -refc)),
+                                     __builtin_amdgcn_exp2f(fmaf(sv[3], scale_log2, -refc)));
+        }
+        pb[pp][rt] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        lacc[rt] = mfma_bf16(ones, pb[pp][rt], lacc[rt]);
+      }
     }
 
-    // ---- PV: O^T += V^T P^T ---------------------------------------------------------
+    // ---- PV: O^T += V^T P^T per 32-key pair -------------------------------------------
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint4 a = *reinterpret_cast<const uint4*>(vt_base + (dt * 16 + col) * kVtStride + quad * 8);
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+    for (int pp = 0; pp < kPairs; ++pp) {
+      bf16x8_t va[DT];
 #pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) o[dt][rt] = mfma_bf16(av, pb[rt], o[dt][rt]);
+      for (int dt = 0; dt < DT; ++dt)
+        va[dt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                                                  vt_base + (dt * 16 + col) * kVtStride + pp * 32 + quad * 8));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int rt = 0; rt < kRowTiles; ++rt) o[dt][rt] = mfma_bf16(va[dt], pb[pp][rt], o[dt][rt]);
     }
   };
 
-  // ---- main loop: both halves in step; tiles past a half's range are skipped ---------
-  Stage sa, sb;
-  load_tile(sa, tile0);
-  load_tile(sb, tile0 + 1);
-  store_tile(sa, 0);
+  // ---- main loop: both halves in step; steps past a half's range are skipped ---------
+  store_tile(load_tile(tile0), 0);
   __syncthreads();
-  for (int i = 0; i < nsteps; i += 2) {
-    // even step: tile tile0+i in buffer 0, tile+1 staged in sb, tile+2 loads into sa
-    load_tile(sa, tile0 + i + 2);
-    if (tile0 + i < tile_end) compute_tile(tile0 + i, 0);
-    store_tile(sb, 1);
-    __syncthreads();
-    if (i + 1 >= nsteps) break;
-    // odd step: tile tile0+i+1 in buffer 1, tile+1 staged in sa, tile+2 loads into sb
-    load_tile(sb, tile0 + i + 3);
-    if (tile0 + i + 1 < tile_end) compute_tile(tile0 + i + 1, 1);
-    store_tile(sa, 0);
+  for (int i = 0; i < nsteps; ++i) {
+    // the next step's loads are in flight while this one computes
+    const Stage nx = load_tile(tile0 + i + 1);
+    if (tile0 + i < tile_end) compute_tile(tile0 + i, i & 1);
+    store_tile(nx, (i + 1) & 1);
     __syncthreads();
   }
 
