@@ -191,6 +191,38 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
                      int32_t D, int32_t block_size, int32_t max_blocks, int32_t max_query_len,
                      float scale, pa_stream_t stream);
 
+/*
+ * Multi-query paged decode for speculative-decoding verification ([mini-llm]
+ * §3.6: the target model checks the K draft tokens in one pass, equivalent to
+ * one prefill).  Sequence b brings NQ consecutive queries (the last accepted
+ * token and NQ - 1 drafts), all already stored in the cache with
+ * pa_cache_store; query i sits at position L_b - NQ + i and attends keys
+ * t <= L_b - NQ + i:
+ *   out[b][i][h][:] = sum_t softmax_t(scale * q[b][i][h] . K_b[t][g]) V_b[t][g].
+ * This is pa_prefill with C_b = NQ for every sequence, computed the way
+ * pa_decode is: one workgroup per (sequence, KV head, partition) serves its
+ * NQ * G (query, head) rows, so each K/V byte is read once; split-K partials
+ * are combined by the same log-sum-exp reduce.
+ *
+ * out, q          bf16 [B][NQ][Hq][D]; out may not alias q.
+ * NQ              1 <= NQ and NQ * (Hq / Hkv) <= 32, else PA_ERR_UNSUPPORTED
+ *                 (NQ = 1 is pa_decode).
+ * context_lens    int32 [B]; L_b >= NQ is a device-side precondition
+ *                 (a query whose position would be negative sees no key and
+ *                 gets zeros); L_b == 0 gives zeros.
+ * other arguments as for pa_decode; the workspace holds fp32 partials
+ * [B][NQ][Hq][P][D] followed by log-sum-exps [B][NQ][Hq][P].
+ */
+size_t pa_decode_multi_workspace_bytes(int32_t B, int32_t NQ, int32_t Hq, int32_t Hkv, int32_t D,
+                                       int32_t max_context_len, int32_t partition_size);
+
+pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                          int32_t NQ, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                          int32_t max_blocks, int32_t max_context_len, float scale,
+                          int32_t partition_size, void* workspace, size_t workspace_bytes,
+                          pa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

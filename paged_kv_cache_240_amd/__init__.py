@@ -22,7 +22,8 @@ import torch
 __all__ = ["load", "PAError", "Call", "cache_store", "decode", "decode_partitions",
            "decode_combine", "prefill", "prepare_cache_store", "prepare_decode",
            "prepare_decode_partitions", "prepare_decode_combine", "prepare_prefill",
-           "decode_workspace_bytes", "decode_partition_size", "BLOCK_SIZE", "library_path",
+           "decode_workspace_bytes", "decode_partition_size", "decode_multi", "prepare_decode_multi",
+           "decode_multi_workspace_bytes", "BLOCK_SIZE", "library_path",
            "STATUS"]
 
 BLOCK_SIZE = 16
@@ -52,6 +53,9 @@ _SIGS = {
     "pa_decode_combine": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p]),
     "pa_prefill": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _i32, _i32, _f32, _p]),
+    "pa_decode_multi_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_multi": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                       _i32, _i32, _f32, _i32, _p, _sz, _p]),
 }
 
 
@@ -226,6 +230,54 @@ def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_c
     return Call("pa_decode", (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                               _ptr(context_lens), B, hq, hkv, d, bs, mb, int(max_context_len),
                               float(scale), P, _ptr(workspace), wbytes, _stream(dev)),
+                result=out, keep=(q, k_cache, v_cache, block_tables, context_lens, workspace))
+
+
+def decode_multi_workspace_bytes(B, NQ, Hq, Hkv, D, max_context_len, partition_size=-1):
+    return int(load().pa_decode_multi_workspace_bytes(B, NQ, Hq, Hkv, D, max_context_len,
+                                                      partition_size))
+
+
+def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                 partition_size=-1, out=None, workspace=None):
+    """Multi-query paged decode for speculative verification (pa_decode_multi).
+
+    q bf16 [B, NQ, Hq, D]: query i of sequence b sits at position L_b - NQ + i and
+    attends keys up to it.  Returns out bf16 [B, NQ, Hq, D].
+    """
+    return prepare_decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale,
+                                max_context_len, partition_size, out, workspace)()
+
+
+def prepare_decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                         partition_size=-1, out=None, workspace=None):
+    """Validated pa_decode_multi call (see decode_multi); allocates out/workspace once."""
+    nb, hkv, bs, d = _cache_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _check(q, "q", torch.bfloat16, 4, dev)
+    B, nq, hq, dq = q.shape
+    if dq != d:
+        raise ValueError("q head_dim differs from the cache's")
+    _check(block_tables, "block_tables", torch.int32, 2, dev)
+    _check(context_lens, "context_lens", torch.int32, 1, dev)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables and context_lens must have one row per sequence")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", torch.bfloat16, 4, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    P = decode_partition_size(B, hkv, max_context_len) if partition_size == -1 else partition_size
+    need = decode_multi_workspace_bytes(B, nq, hq, hkv, d, max_context_len, P) if P > 0 else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check(workspace, "workspace", workspace.dtype, None, dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return Call("pa_decode_multi", (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(block_tables), _ptr(context_lens), B, nq, hq, hkv, d, bs,
+                                    block_tables.shape[1], int(max_context_len), float(scale), P,
+                                    _ptr(workspace), wbytes, _stream(dev)),
                 result=out, keep=(q, k_cache, v_cache, block_tables, context_lens, workspace))
 
 

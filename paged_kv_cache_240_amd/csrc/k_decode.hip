@@ -344,7 +344,8 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
 }
 
 // Log-sum-exp combine of split-K partials (Flash Decode's reduce): one wave
-// per (query head, sequence).  Every load is issued before L is known: lane
+// per (query row, sequence), a row being a query head (or, for multi-query
+// decode, a (query, head) pair).  Every load is issued before L is known: lane
 // j < num_parts reads lse[j] and each lane reads one 16-byte piece of every
 // partial it may need (indices clamped into the workspace); partitions past
 // ceil(L / P) were never written and are removed by selects, not arithmetic,
@@ -381,6 +382,10 @@ combine_kernel(uint16_t* __restrict__ out, const float* __restrict__ o_part,
   }
   const int n = (L + part_tokens - 1) / part_tokens;
   const float M = wave_max(lane < n ? my_lse : -INFINITY);
+  if (M == -INFINITY) {  // no partition saw a key of this row (multi-query rows before the cache)
+    if (sub == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
+    return;
+  }
   const float W = wave_sum(lane < n ? exp2f(my_lse - M) : 0.f);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -424,6 +429,10 @@ combine_many_kernel(uint16_t* __restrict__ out, const float* __restrict__ o_part
   float M = -INFINITY;
   for (int i = lane; i < n; i += 64) M = fmaxf(M, ls[i]);
   M = wave_max(M);
+  if (M == -INFINITY) {  // no partition saw a key of this row
+    if (sub == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
+    return;
+  }
   float W = 0.f;
   for (int i = lane; i < n; i += 64) W += exp2f(ls[i] - M);
   W = wave_sum(W);

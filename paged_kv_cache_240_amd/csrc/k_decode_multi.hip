@@ -1,0 +1,416 @@
+// Multi-query paged decode for gfx950: speculative-decoding verification.
+//
+// Operation (mini-llm-engine post, §3.6: the target model checks the K draft
+// tokens in one pass, equivalent to one prefill; §3.1: K/V in 16-token
+// physical blocks behind a block table; Pico-vLLM write-up, §1: GQA): each
+// sequence b brings NQ consecutive queries (the last accepted token and the
+// drafts), already stored in the cache, so query i sits at position
+// L_b - NQ + i and attends keys t <= L_b - NQ + i:
+//   out[b,i,h] = softmax(scale * q[b,i,h] K_b^T) V_b   (causal over the NQ rows).
+//
+// It is the decode kernel's layout with NQ * G (query, head) rows instead of G
+// heads: one workgroup per (sequence, KV head, partition) reads every K/V byte
+// once for all its rows.  Rows r = i * G + h fill up to two 16-row MFMA tiles
+// (CT).  Workgroup = 4 waves; a partition of up to 512 tokens is walked in
+// chunks of 32 blocks, wave w taking blocks w, w+4, ..., w+28, as block pairs
+// in the order K(2j), K(2j+1), V(2j), V(2j+1) through a 4-slot register ring
+// (loads run one pair ahead).  Per pair and row tile:
+//   QK   S^T = K Q^T (v_mfma_f32_16x16x32_bf16, K straight from memory as the
+//        A operand, the tile's query rows as the B operand); keys past the
+//        row's causal limit or the range become -inf by a select.
+//   P    the pair's max per row (4 lanes per row: two cross-row swaps); the
+//        row's reference max is raised only when the pair exceeds it by more
+//        than 2^8 (then the accumulators are rescaled), so p = 2^((s - m) *
+//        scale * log2 e) stays below 256; rounded to bf16 in place, the 8 p of
+//        a lane are its A operand of PV.
+//   PV   O = P V: V rows paired per dim with v_perm into B operands shared by
+//        the row tiles; a product against a ones operand accumulates l from
+//        the same rounded p.  V rows past the range are redirected to row 0 of
+//        their block at load time (finite data under p = 0).
+// The waves meet once, at the end, through LDS.  Split-K partials are the
+// normalised fp32 rows plus base-2 log-sum-exps, reduced by the decode
+// combine kernel over NQ * Hq rows per sequence; a row without a visible key in
+// a partition writes zeros and lse = -inf.
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kWaveBlocks = 8;                           // blocks per wave per chunk
+constexpr int kChunkTokens = kWaves * kWaveBlocks * kBlockSize;  // 512
+constexpr int kDepth = 4;                                // ring slots: one block pair of K and V
+constexpr float kLazyLog2 = 8.f;                         // reference max may lag by 2^8
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4_t mfma_bf16(uint4 a, uint4 b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  const bf16x2_t r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Ring step s of a chunk (0..15): block pair s / 4; s % 4 = K(2j), K(2j+1), V(2j), V(2j+1).
+__host__ __device__ constexpr int step_block(int s) { return 2 * (s / 4) + (s % 2); }
+__host__ __device__ constexpr bool step_is_v(int s) { return (s % 4) >= 2; }
+
+// ONE: the range is a single chunk (partitions of at most 512 tokens): no
+// refills past it.
+// Two row tiles with a ring that cycles over chunks need more than the 256
+// registers of two waves per SIMD: that variant runs one wave per SIMD.
+template <int D, int G, int CT, bool SPLIT, bool ONE>
+__global__ void __launch_bounds__(256, (CT == 2 && !ONE) ? 1 : 2)
+decode_multi_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+                    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+                    const int32_t* __restrict__ context_lens, int NQ, int Hkv, int max_blocks,
+                    float scale_log2, int part_tokens, int num_parts, uint16_t* __restrict__ out,
+                    float* __restrict__ o_part, float* __restrict__ lse) {
+  static_assert(CT == 1 || CT == 2, "one or two 16-row tiles");
+  constexpr int KS = D / 32;    // QK k-steps over the head dimension
+  constexpr int DPL = D / 16;   // PV: dims per lane = output tiles of 16 columns
+  constexpr int HALF = DPL / 2; // dwords of one V row piece
+  constexpr int SLOT = 4 * KS;  // dwords per lane of a K block
+  static_assert(SLOT == 4 * HALF, "K and V blocks must occupy the same ring slot");
+  constexpr int STEPS = 2 * kWaveBlocks;
+  constexpr int ROWS = 16 * CT;
+
+  __shared__ __align__(16) float red[kWaves][ROWS][D];  // per-wave outputs, dim n*DPL+s at s*16+n
+  __shared__ float st_m[kWaves][ROWS], st_l[kWaves][ROWS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int Hq = Hkv * G;
+  const int hq0 = g * G;
+  const int R = NQ * G;  // valid rows
+  const int32_t* bt_row = block_tables + (int64_t)b * max_blocks;
+  const int L = context_lens[b];
+  // first chunk's table entries requested before L is known (clamped; an entry
+  // past the sequence is replaced by the range's first block once L arrives)
+  const int lb0 = SPLIT ? p * part_tokens / kBlockSize : 0;
+  const int lb_spec = lb0 + wave + kWaves * (threadIdx.x & 7);
+  const int ent_spec = bt_row[min(lb_spec, max_blocks - 1)];
+  const int ent_first = bt_row[lb0];
+  const int col = lane & 15, quad = lane >> 4;
+
+  // this lane's rows (one per tile, the S^T column): query row and causal limit
+  uint4 qraw[CT][KS];
+  int qrow_i[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int r = min(ct * 16 + col, R - 1);  // padding lanes read a valid row, then zero it
+    qrow_i[ct] = r / G;
+    const uint16_t* qrow = q + (((int64_t)b * NQ + r / G) * Hq + hq0 + r % G) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[ct][ks] = *reinterpret_cast<const uint4*>(qrow + ks * 32 + quad * 8);
+  }
+  asm volatile("" ::"v"(ent_spec), "s"(ent_first), "s"(L));
+
+  int t_begin = 0, t_end = L;
+  if (SPLIT) {
+    t_begin = p * part_tokens;
+    if (t_begin >= L) return;  // empty partition: not written, not combined
+    t_end = min(t_begin + part_tokens, L);
+  } else if (L <= 0) {
+    for (int e = threadIdx.x; e < R * D / 2; e += blockDim.x) {
+      const int r = e / (D / 2);
+      reinterpret_cast<uint32_t*>(out + (((int64_t)b * NQ + r / G) * Hq + hq0 + r % G) * D)[e % (D / 2)] = 0u;
+    }
+    return;
+  }
+
+  uint4 qb[CT][KS];
+  int lim[CT];  // exclusive bound on the keys a row sees inside the range
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const bool valid = ct * 16 + col < R;
+    lim[ct] = valid ? min(t_end, L - NQ + qrow_i[ct] + 1) : t_begin;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ct][ks] = valid ? qraw[ct][ks] : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  floatx4_t o[CT][DPL];  // O[row 16ct + 4quad + e][dim col*DPL + s] in o[ct][s][e]
+  floatx4_t lacc[CT];
+  float m_ref[CT];  // reference max of the lane's row (raw scores; -inf: none seen)
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    lacc[ct] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    m_ref[ct] = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < DPL; ++s) o[ct][s] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const float lazy_raw = kLazyLog2 / scale_log2;
+
+  const int64_t head_off = (int64_t)g * kBlockSize * D;
+  const int64_t blk_stride = (int64_t)Hkv * kBlockSize * D;
+  const int nchunks = ONE ? 1 : (t_end - t_begin + kChunkTokens - 1) / kChunkTokens;
+  const int last_lb = (t_end - 1) / kBlockSize;
+  const int lane_k = col * D + quad * 8;
+  const int lane_v = col * DPL;
+  const uint4 ones = make_uint4(kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2);
+
+  auto fetch_entries = [&](int c) -> int {
+    const int lb = (t_begin + c * kChunkTokens) / kBlockSize + wave + kWaves * (lane & 7);
+    return bt_row[min(lb, last_lb)];
+  };
+  // ring step `step` of the chunk whose entries are `ent`; `left` = rows of that block in range
+  auto load_step = [&](uint32_t (&slot)[SLOT], int ent, int step, int left) {
+    const int i = step_block(step);
+    const int64_t base = (int64_t)__builtin_amdgcn_readlane(ent, i) * blk_stride + head_off;
+    if (!step_is_v(step)) {
+      const uint16_t* src = k_cache + base + lane_k;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 t = load_stream16(src + ks * 32);
+        slot[4 * ks] = t.x; slot[4 * ks + 1] = t.y; slot[4 * ks + 2] = t.z; slot[4 * ks + 3] = t.w;
+      }
+    } else {
+      const uint16_t* src = v_cache + base + lane_v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * quad + r < left ? 4 * quad + r : 0;
+        if constexpr (HALF == 4) {
+          const uint4 t = load_stream16(src + row * D);
+          slot[4 * r] = t.x; slot[4 * r + 1] = t.y; slot[4 * r + 2] = t.z; slot[4 * r + 3] = t.w;
+        } else {
+          const uint2 t = load_stream8(src + row * D);
+          slot[2 * r] = t.x; slot[2 * r + 1] = t.y;
+        }
+      }
+    }
+  };
+  auto rows_left = [&](int nt, int step) {
+    return nt - (wave + kWaves * step_block(step)) * kBlockSize;
+  };
+
+  int ent_cur = lb_spec <= last_lb ? ent_spec : ent_first;  // == fetch_entries(0)
+  int ent_nxt = ONE ? 0 : fetch_entries(nchunks > 1 ? 1 : 0);
+  const int nt0 = min(kChunkTokens, t_end - t_begin);
+  uint32_t ring[kDepth][SLOT];
+#pragma unroll
+  for (int s = 0; s < kDepth; ++s) load_step(ring[s], ent_cur, s, rows_left(nt0, s));
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int c0 = t_begin + c * kChunkTokens;
+    const int nt = min(kChunkTokens, t_end - c0);
+    const int nt_next = min(kChunkTokens, t_end - c0 - kChunkTokens);
+    floatx4_t st[2][CT];  // raw scores of the pair: keys 4*quad+e of its two blocks
+    uint4 pa[CT];         // bf16 probabilities of the pair (PV A operand)
+
+    static_for<STEPS>([&](auto step_c) {
+      constexpr int step = decltype(step_c)::value;
+      uint32_t(&cur)[SLOT] = ring[step % kDepth];
+      constexpr int i = step_block(step);
+
+      if constexpr (!step_is_v(step)) {
+        // ---- QK on block i ----------------------------------------------------------
+        constexpr int h = step % 2;  // first or second block of the pair
+        const int kb = c0 + (wave + kWaves * i) * kBlockSize + 4 * quad;  // key of element 0
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            acc = mfma_bf16(make_uint4(cur[4 * ks], cur[4 * ks + 1], cur[4 * ks + 2], cur[4 * ks + 3]),
+                            qb[ct][ks], acc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st[h][ct][e] = kb + e < lim[ct] ? acc[e] : -INFINITY;
+        }
+        constexpr int ns = step + kDepth;
+        if constexpr (ns < STEPS) load_step(cur, ent_cur, ns, rows_left(nt, ns));
+        else if constexpr (!ONE) load_step(cur, ent_nxt, ns - STEPS, rows_left(nt_next, ns - STEPS));
+
+        if constexpr (h == 1) {
+          // ---- P: the pair's probabilities against a lazily raised reference ------------
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            float mx = fmaxf(fmaxf(fmaxf(st[0][ct][0], st[0][ct][1]), fmaxf(st[0][ct][2], st[0][ct][3])),
+                             fmaxf(fmaxf(st[1][ct][0], st[1][ct][1]), fmaxf(st[1][ct][2], st[1][ct][3])));
+            mx = fmaxf(mx, swap16(mx));
+            mx = fmaxf(mx, swap32(mx));
+            const bool raise = mx > m_ref[ct] + lazy_raw;  // false for -inf pairs
+            if (__builtin_amdgcn_ballot_w64(raise)) {
+              const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref[ct] - mx) * scale_log2) : 1.f;
+              m_ref[ct] = raise ? mx : m_ref[ct];
+              // accumulator lane (col, quad) holds rows 4*quad+e: their alphas live in lanes 4*quad+e
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float a = __shfl(alpha, 4 * quad + e);
+                lacc[ct][e] *= a;
+#pragma unroll
+                for (int s = 0; s < DPL; ++s) o[ct][s][e] *= a;
+              }
+            }
+            const float refc = m_ref[ct] == -INFINITY ? 0.f : m_ref[ct] * scale_log2;
+            pa[ct].x = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(st[0][ct][0], scale_log2, -refc)),
+                                  __builtin_amdgcn_exp2f(fmaf(st[0][ct][1], scale_log2, -refc)));
+            pa[ct].y = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(st[0][ct][2], scale_log2, -refc)),
+                                  __builtin_amdgcn_exp2f(fmaf(st[0][ct][3], scale_log2, -refc)));
+            pa[ct].z = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(st[1][ct][0], scale_log2, -refc)),
+                                  __builtin_amdgcn_exp2f(fmaf(st[1][ct][1], scale_log2, -refc)));
+            pa[ct].w = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(st[1][ct][2], scale_log2, -refc)),
+                                  __builtin_amdgcn_exp2f(fmaf(st[1][ct][3], scale_log2, -refc)));
+          }
+        }
+      } else if constexpr (step % 2 == 1) {
+        // ---- PV on the pair ----------------------------------------------------------------
+        uint32_t(&va)[SLOT] = ring[(step - 1) % kDepth];
+        uint32_t(&vb)[SLOT] = cur;
+#pragma unroll
+        for (int s = 0; s < DPL; ++s) {
+          const int w = s / 2;
+          uint4 bv;
+          if (s % 2 == 0) {
+            bv.x = interleave_lo(va[w], va[HALF + w]);
+            bv.y = interleave_lo(va[2 * HALF + w], va[3 * HALF + w]);
+            bv.z = interleave_lo(vb[w], vb[HALF + w]);
+            bv.w = interleave_lo(vb[2 * HALF + w], vb[3 * HALF + w]);
+          } else {
+            bv.x = interleave_hi(va[w], va[HALF + w]);
+            bv.y = interleave_hi(va[2 * HALF + w], va[3 * HALF + w]);
+            bv.z = interleave_hi(vb[w], vb[HALF + w]);
+            bv.w = interleave_hi(vb[2 * HALF + w], vb[3 * HALF + w]);
+          }
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) o[ct][s] = mfma_bf16(pa[ct], bv, o[ct][s]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) lacc[ct] = mfma_bf16(pa[ct], ones, lacc[ct]);
+        constexpr int na = step - 1 + kDepth, nb = step + kDepth;
+        if constexpr (nb < STEPS) {
+          load_step(va, ent_cur, na, rows_left(nt, na));
+          load_step(vb, ent_cur, nb, rows_left(nt, nb));
+        } else if constexpr (!ONE) {
+          load_step(va, ent_nxt, na - STEPS, rows_left(nt_next, na - STEPS));
+          load_step(vb, ent_nxt, nb - STEPS, rows_left(nt_next, nb - STEPS));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (!ONE) {
+      ent_cur = ent_nxt;
+      ent_nxt = fetch_entries(c + 2 < nchunks ? c + 2 : nchunks - 1);
+    }
+  }
+
+  // ---- combine the waves through LDS, write ----------------------------------------
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = ct * 16 + 4 * quad + e;
+      if (row < R) {
+#pragma unroll
+        for (int s = 0; s < DPL; ++s) red[wave][row][s * 16 + col] = o[ct][s][e];
+        if (col == 0) st_l[wave][row] = lacc[ct][e];
+      }
+    }
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+    if (quad == 0 && ct * 16 + col < R)
+      st_m[wave][ct * 16 + col] = m_ref[ct] == -INFINITY ? -INFINITY : m_ref[ct] * scale_log2;
+  __syncthreads();
+  for (int e = threadIdx.x; e < R * D / 4; e += blockDim.x) {
+    const int r = e / (D / 4);
+    const int d4 = (e % (D / 4)) * 4;
+    const int n = d4 / DPL, s0 = d4 % DPL;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, st_m[w][r]);
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = st_m[w][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st_m[w][r] - M);
+      const float* rr = &red[w][r][s0 * 16 + n];
+      sum.x += wt * rr[0]; sum.y += wt * rr[16]; sum.z += wt * rr[32]; sum.w += wt * rr[48];
+      lsum += wt * st_l[w][r];
+    }
+    // a row without a visible key here contributes nothing: zeros, lse -inf
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const int64_t grow = ((int64_t)b * NQ + r / G) * Hq + hq0 + r % G;
+    if (SPLIT) {
+      *reinterpret_cast<float4*>(o_part + (grow * num_parts + p) * D + d4) =
+          make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
+      if (d4 == 0) lse[grow * num_parts + p] = lsum > 0.f ? M + log2f(lsum) : -INFINITY;
+    } else {
+      uint2 ov;
+      ov.x = pack_bf16x2(sum.x * inv, sum.y * inv);
+      ov.y = pack_bf16x2(sum.z * inv, sum.w * inv);
+      *reinterpret_cast<uint2*>(out + grow * D + d4) = ov;
+    }
+  }
+}
+
+template <int D, int G, int CT>
+hipError_t launch_g(void* out, float* o_part, float* lse, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* bt, const int32_t* cl, int B, int NQ,
+                    int Hkv, int mb, int mcl, float scale, int P, hipStream_t stream) {
+  const float sl = scale * 1.4426950408889634f;
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const auto* kc = static_cast<const uint16_t*>(k_cache);
+  const auto* vc = static_cast<const uint16_t*>(v_cache);
+  auto* oo = static_cast<uint16_t*>(out);
+  if (P > 0) {
+    const int np = (mcl + P - 1) / P;
+    if (P <= kChunkTokens)
+      hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, true, true>), dim3(np, Hkv, B), dim3(256), 0,
+                         stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, P, np, oo, o_part, lse);
+    else
+      hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, true, false>), dim3(np, Hkv, B), dim3(256), 0,
+                         stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, P, np, oo, o_part, lse);
+  } else {
+    hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, false, false>), dim3(1, Hkv, B), dim3(256), 0,
+                       stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, 0, 1, oo, o_part, lse);
+  }
+  return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_ct(void* out, float* o_part, float* lse, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* bt, const int32_t* cl, int B, int NQ,
+                     int Hkv, int mb, int mcl, float scale, int P, hipStream_t stream) {
+  if (NQ * G <= 16)
+    return launch_g<D, G, 1>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, NQ, Hkv, mb, mcl, scale, P, stream);
+  return launch_g<D, G, 2>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, NQ, Hkv, mb, mcl, scale, P, stream);
+}
+
+template <int D>
+hipError_t launch_d(int G, void* out, float* o_part, float* lse, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* bt, const int32_t* cl, int B, int NQ,
+                    int Hkv, int mb, int mcl, float scale, int P, hipStream_t st) {
+  switch (G) {
+#define PA_MULTI_G(GG) \
+    case GG: return launch_ct<D, GG>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, NQ, Hkv, mb, mcl, scale, P, st);
+    PA_MULTI_G(1) PA_MULTI_G(2) PA_MULTI_G(3) PA_MULTI_G(4)
+    PA_MULTI_G(5) PA_MULTI_G(6) PA_MULTI_G(7) PA_MULTI_G(8)
+#undef PA_MULTI_G
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_multi(void* out, float* o_part, float* lse, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens, int B,
+                               int NQ, int Hq, int Hkv, int D, int max_blocks, int max_context_len,
+                               float scale, int partition_size, hipStream_t stream) {
+  const int G = Hq / Hkv;
+  if (D == 128)
+    return launch_d<128>(G, out, o_part, lse, q, k_cache, v_cache, block_tables, context_lens, B,
+                         NQ, Hkv, max_blocks, max_context_len, scale, partition_size, stream);
+  return launch_d<64>(G, out, o_part, lse, q, k_cache, v_cache, block_tables, context_lens, B, NQ,
+                      Hkv, max_blocks, max_context_len, scale, partition_size, stream);
+}
+
+}  // namespace pa

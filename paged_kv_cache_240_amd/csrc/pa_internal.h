@@ -21,6 +21,15 @@ hipError_t launch_decode(void* out, float* o_part, float* lse, const void* q, co
                          int max_blocks, int max_context_len, float scale, int partition_size,
                          hipStream_t stream);
 
+// Multi-query (speculative verification) partial kernel or single pass: q/out
+// are [B][NQ][Hq][D]; the partials are reduced by launch_decode_combine over
+// NQ * Hq rows per sequence.
+hipError_t launch_decode_multi(void* out, float* o_part, float* lse, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens, int B,
+                               int NQ, int Hq, int Hkv, int D, int max_blocks, int max_context_len,
+                               float scale, int partition_size, hipStream_t stream);
+
 hipError_t launch_decode_combine(void* out, const float* o_part, const float* lse,
                                  const int32_t* context_lens, int B, int Hq, int D,
                                  int num_partitions, int partition_size, hipStream_t stream);

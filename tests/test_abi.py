@@ -27,6 +27,7 @@ def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("pa_cache_store", "pa_decode", "pa_decode_partitions", "pa_decode_combine",
               "pa_decode_workspace_bytes", "pa_decode_partition_size", "pa_prefill",
+              "pa_decode_multi", "pa_decode_multi_workspace_bytes",
               "pa_status_str"):
         assert s in syms
 
@@ -128,3 +129,32 @@ def test_prefill_validation(kw, code):
     a.update(kw)
     assert pa.load().pa_prefill(a["out"], P, P, P, P, P, a["qsl"], a["B"], a["T"], a["Hq"],
                                 a["Hkv"], a["D"], a["bs"], a["mb"], a["mql"], 0.1, None) == code
+
+
+def _multi(**kw):
+    a = dict(out=P, q=P, kc=P, vc=P, bt=P, cl=P, B=2, NQ=5, Hq=12, Hkv=2, D=128, bs=16, mb=8,
+             mcl=128, scale=0.088, ps=64, ws=None, wsb=0)
+    a.update(kw)
+    return pa.load().pa_decode_multi(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["B"],
+                                     a["NQ"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["mb"], a["mcl"],
+                                     a["scale"], a["ps"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), NULL), (dict(q=None), NULL), (dict(bt=None), NULL), (dict(cl=None), NULL),
+    (dict(NQ=0), SHAPE), (dict(NQ=-2), SHAPE), (dict(NQ=6), UNSUP), (dict(Hq=16, Hkv=2, NQ=5), UNSUP),
+    (dict(Hq=8, Hkv=1, NQ=4, B=0), OK), (dict(D=80), UNSUP), (dict(bs=32), UNSUP),
+    (dict(mcl=129), SHAPE), (dict(ps=24), SHAPE), (dict(ps=-2), SHAPE),
+    (dict(ps=64, ws=None), WS), (dict(ps=64, ws=P, wsb=100), WS), (dict(B=0), OK),
+])
+def test_decode_multi_validation(kw, code):
+    assert _multi(**kw) == code
+
+
+def test_decode_multi_workspace_is_per_query_decode_workspace():
+    lib = pa.load()
+    for B, NQ, L, P in [(16, 5, 8192, 512), (3, 2, 100, 16), (1, 1, 2048, 64)]:
+        one = lib.pa_decode_workspace_bytes(B, 12, 2, 128, L, P)
+        assert lib.pa_decode_multi_workspace_bytes(B, NQ, 12, 2, 128, L, P) == NQ * one
+        assert one == B * 12 * (-(-L // P)) * 129 * 4
+    assert lib.pa_decode_multi_workspace_bytes(4, 0, 12, 2, 128, 100, 16) == 0

@@ -265,6 +265,26 @@ def prefill_batch(prefix_lens, chunk_lens, Hq, Hkv, D, num_blocks, seed, theta=1
     )
 
 
+def verify_batch(lens, nq, Hq, Hkv, D, num_blocks, seed, theta=1e6, poison=False, table_fill=-1,
+                 device="cpu", name=""):
+    """A speculative-verification step: sequence b has lens[b] tokens of which
+    the last nq (the last accepted token and nq - 1 drafts) are new and go
+    through the store; q viewed as [B, nq, Hq, D] holds their queries."""
+    lens = np.asarray(lens, dtype=np.int64)
+    return prefill_batch(lens - nq, [nq] * len(lens), Hq, Hkv, D, num_blocks, seed, theta=theta,
+                         poison=poison, table_fill=table_fill, device=device, name=name)
+
+
+def spec_verify(seed=2406, device="cpu", batch=16, context=8192, nq=5, poison=False):
+    """Verification of 4 draft tokens (5 queries per sequence) at the Qwen2.5-1.5B head
+    shape: 16 sequences of 8192 tokens, 16-token blocks dealt from a pool of exactly the
+    blocks needed."""
+    nb = batch * (-(-context // 16))
+    return verify_batch([context] * batch, nq, QWEN_HQ, QWEN_HKV, QWEN_D, nb, seed, theta=1e6,
+                        poison=poison, device=device,
+                        name=f"spec verify {batch}x{context}, {nq} queries")
+
+
 # --------------------------------------------------------------------------
 # The five workloads at their stated sizes.
 # --------------------------------------------------------------------------
