@@ -150,6 +150,37 @@ def run_long(layers, steps, warmup):
     return step_ms, kernel_ms * 1000 / len(L), decode_only_ms
 
 
+def run_verify(layers, steps, warmup, nq=5):
+    """Speculative verification over the same 28 layer caches: nq queries per
+    sequence (the last accepted token and nq-1 drafts) through pa_decode_multi
+    with 512-token partitions, one call per layer, back to back (cold caches)."""
+    gen = torch.Generator(device=layers[0].q.device)
+    gen.manual_seed(2407)
+    calls = []
+    for b in layers:
+        q = torch.randn((b.B, nq, b.Hq, b.D), generator=gen, device=b.q.device).to(torch.bfloat16)
+        calls.append(pa.prepare_decode_multi(q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
+                                             b.scale, b.max_context_len, LONG_P))
+
+    def run():
+        for c in calls:
+            c()
+    for _ in range(warmup):
+        run()
+    _sync()
+    t0, t1 = _event(), _event()
+    t0.record()
+    for _ in range(steps):
+        run()
+    t1.record()
+    _sync()
+    us = t0.elapsed_time(t1) * 1000 / steps / len(layers)
+    kv = W.kv_bytes_logical(layers[0].context_lens.cpu().numpy(), layers[0].Hkv, layers[0].D)
+    return {"queries_per_sequence": nq, "us_per_layer_call": round(us, 2),
+            "kv_GBps": round(kv / us / 1e3, 1), "pct_of_hbm_peak": round(kv / us / 1e3 / HBM_PEAK_GBPS * 100, 2),
+            "note": "pa_decode_multi, partitions of 512 + combine, 28 layer caches of 16 x 8192 tokens"}
+
+
 # ---------------------------------------------------------------------------
 # Context measurements (the other decode shapes and the prefill)
 # ---------------------------------------------------------------------------
@@ -213,6 +244,33 @@ def run_context(device):
                               "prefill_TFLOPs": round(flops / us_pre / 1e6, 1),
                               "mfma_bf16_frac": round(flops / us_pre / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
                               "flop": flops}
+    return res
+
+
+def run_blocks(device):
+    """Copy-on-write and swap of whole blocks at the Qwen2.5-1.5B head shape (8 KiB per
+    block and pool): 2048 device-to-device copies, and 1024 blocks out to pinned host
+    memory and back (over PCIe).  Rates count bytes read plus bytes written."""
+    nb, hkv, d = 8192, W.QWEN_HKV, W.QWEN_D
+    kc = torch.randn((nb, hkv, 16, d), device=device).to(torch.bfloat16)
+    vc = torch.randn((nb, hkv, 16, d), device=device).to(torch.bfloat16)
+    g = torch.Generator().manual_seed(2408)
+    perm = torch.randperm(nb, generator=g).to(torch.int32)
+    src, dst = perm[:2048].to(device), perm[4096:6144].to(device)
+    cow = pa.prepare_copy_blocks(kc, vc, src, dst)
+    blk = hkv * 16 * d * 2
+    us = time_calls(cow, 50)
+    res = {"cow_2048_blocks_us": round(us, 2), "cow_GBps": round(2 * 2 * 2048 * blk / us / 1e3, 1)}
+    hk = torch.empty((1024, hkv, 16, d), dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty((1024, hkv, 16, d), dtype=torch.bfloat16).pin_memory()
+    slots = torch.arange(1024, dtype=torch.int32, device=device)
+    seq = perm[:1024].to(device)
+    out_ = pa.prepare_swap_blocks(hk, hv, kc, vc, seq, slots)
+    in_ = pa.prepare_swap_blocks(kc, vc, hk, hv, slots, perm[6144:7168].to(device))
+    us_out, us_in = time_calls(out_, 20, warm=3), time_calls(in_, 20, warm=3)
+    moved = 2 * 1024 * blk
+    res.update({"swap_out_1024_blocks_us": round(us_out, 1), "swap_out_GBps": round(moved / us_out / 1e3, 2),
+                "swap_in_1024_blocks_us": round(us_in, 1), "swap_in_GBps": round(moved / us_in / 1e3, 2)})
     return res
 
 
@@ -393,6 +451,8 @@ def main():
     }
     if not args.no_context:
         line["context"] = run_context(dev)
+        line["context"]["spec_verify_16x8192"] = run_verify(layers, args.steps, args.warmup)
+        line["context"]["block_copies"] = run_blocks(dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layers, args.cpu_budget)
     else:

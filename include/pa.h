@@ -57,7 +57,8 @@ typedef enum {
   PA_ERR_SHAPE = 2,        /* a size is negative, zero where it may not be, or inconsistent */
   PA_ERR_UNSUPPORTED = 3,  /* consistent, but a shape this library does not implement */
   PA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required */
-  PA_ERR_HIP = 5           /* the HIP runtime reported an error while enqueueing */
+  PA_ERR_HIP = 5,          /* the HIP runtime reported an error while enqueueing */
+  PA_ERR_MEMORY = 6        /* a pool is neither device memory nor device-accessible pinned host memory */
 } pa_status;
 
 /* Static, human-readable name of a status code.  Never NULL. */
@@ -222,6 +223,46 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
                           int32_t max_blocks, int32_t max_context_len, float scale,
                           int32_t partition_size, void* workspace, size_t workspace_bytes,
                           pa_stream_t stream);
+
+/*
+ * Copy-on-write block copies inside one pair of pools ([mini-llm] §3.4: a
+ * block shared by several sequences, ref_count > 1, is copied to a freshly
+ * allocated block before one of them writes it).  For every i < n, the whole
+ * [Hkv][block_size][D] tile of block src_blocks[i] is copied, bit for bit, to
+ * block dst_blocks[i], in k_cache and in v_cache.
+ *
+ * k_cache, v_cache         bf16 [num_blocks][Hkv][block_size][D], device memory.
+ * src_blocks, dst_blocks   int32 [n], device memory (or device-accessible
+ *                          pinned host memory); may be NULL when n == 0.
+ * Device-side preconditions: every id is in [0, num_blocks); the destination
+ * ids are distinct and none is also a source (copies run in no fixed order).
+ * PA_ERR_MEMORY if a pointer is neither device memory nor device-accessible
+ * pinned host memory (pageable memory is refused before any launch).
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks,
+                         const int32_t* dst_blocks, int32_t n, int32_t Hkv, int32_t D,
+                         int32_t block_size, int64_t num_blocks, pa_stream_t stream);
+
+/*
+ * Block moves between two pairs of pools: swap-out to and swap-in from host
+ * memory ([mini-llm] §3.5: a preempted sequence's blocks go to CPU memory and
+ * come back into newly allocated device blocks instead of being recomputed).
+ * For every i < n:  dst_k[dst_blocks[i]] = src_k[src_blocks[i]] and the same
+ * for V, whole [Hkv][block_size][D] tiles, bit for bit.
+ *
+ * dst_k, dst_v, src_k, src_v  bf16 pools [*][Hkv][block_size][D]; each either
+ *                             device memory or pinned host memory the device
+ *                             can access (e.g. hipHostMalloc): a kernel moves
+ *                             the data over PCIe, so device-to-host,
+ *                             host-to-device and device-to-device all work.
+ * src_blocks, dst_blocks      int32 [n], device or pinned host memory; may be
+ *                             NULL when n == 0.
+ * Device-side preconditions: ids in range of their pools; destination ids
+ * distinct; the source and destination tiles do not overlap.
+ */
+pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                         const int32_t* src_blocks, const int32_t* dst_blocks, int32_t n,
+                         int32_t Hkv, int32_t D, int32_t block_size, pa_stream_t stream);
 
 #ifdef __cplusplus
 }

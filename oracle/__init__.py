@@ -13,7 +13,9 @@ Sources (the four pages this work follows, cited by title and section):
     section (Flash Decode).
   * "mini-llm-engine" post (liangqianxing): §3.1 Paged KV Cache (16-token
     blocks, per-sequence logical->physical block table), §3.3 Chunked Prefill
-    (prefill ranges), §3.4 Prefix Caching (shared blocks, ref_count > 1).
+    (prefill ranges), §3.4 Prefix Caching (shared blocks, ref_count > 1,
+    copy-on-write), §3.5 CPU Swap, §3.6 Speculative Decoding (verification
+    is a prefill of the draft rows).
   * "nano-vllm" commentary (ai-stack), FAQ Q2 (logical-to-physical block map).
   * "LLM-Inference-Engine" write-up (zingnex forum), "dynamic request injection"
     (prefill is compute-bound, decode is bandwidth-bound).
@@ -23,14 +25,16 @@ Modules:
   store      fused rotate-half RoPE + slot-mapped scatter into the block pool,
              in a pinned fp32 operation order (bit-exact target).
   attention  fp64 paged attention: decode, split-K partials + log-sum-exp
-             combine, and causal chunked prefill.
+             combine, and causal chunked prefill (multi-query verification is
+             the chunked prefill with chunks of NQ rows).
+  blocks     whole-block copies between pools (copy-on-write, swap).
 
 Every function here is pinned by ``tests/test_oracle.py`` against something
 other than itself (closed forms, library routines, invariants, brute force).
 No function of this package is "parity unpinned".
 """
 
-from . import bf16, store, attention  # noqa: F401
+from . import bf16, store, attention, blocks  # noqa: F401
 from .bf16 import (  # noqa: F401
     bf16_to_f32,
     bf16_to_f64,
@@ -48,3 +52,4 @@ from .attention import (  # noqa: F401
     decode_split,
     prefill,
 )
+from .blocks import copy_blocks  # noqa: F401

@@ -23,14 +23,15 @@ __all__ = ["load", "PAError", "Call", "cache_store", "decode", "decode_partition
            "decode_combine", "prefill", "prepare_cache_store", "prepare_decode",
            "prepare_decode_partitions", "prepare_decode_combine", "prepare_prefill",
            "decode_workspace_bytes", "decode_partition_size", "decode_multi", "prepare_decode_multi",
-           "decode_multi_workspace_bytes", "BLOCK_SIZE", "library_path",
+           "decode_multi_workspace_bytes", "copy_blocks", "swap_blocks", "prepare_copy_blocks",
+           "prepare_swap_blocks", "BLOCK_SIZE", "library_path",
            "STATUS"]
 
 BLOCK_SIZE = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpa.so")
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
-          4: "PA_ERR_WORKSPACE", 5: "PA_ERR_HIP"}
+          4: "PA_ERR_WORKSPACE", 5: "PA_ERR_HIP", 6: "PA_ERR_MEMORY"}
 
 _lib = None
 
@@ -54,6 +55,8 @@ _SIGS = {
     "pa_prefill": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _i32, _i32, _f32, _p]),
     "pa_decode_multi_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_copy_blocks": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _p]),
+    "pa_swap_blocks": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
     "pa_decode_multi": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _i32, _f32, _i32, _p, _sz, _p]),
 }
@@ -279,6 +282,65 @@ def prepare_decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale,
                                     block_tables.shape[1], int(max_context_len), float(scale), P,
                                     _ptr(workspace), wbytes, _stream(dev)),
                 result=out, keep=(q, k_cache, v_cache, block_tables, context_lens, workspace))
+
+
+def _pool_dims(t, name):
+    """A [num_blocks, Hkv, 16, D] bf16 pool on the device or in pinned host memory."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 4:
+        raise ValueError(f"{name} must be a bf16 [num_blocks, Hkv, 16, D] tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda" and not t.is_pinned():
+        raise ValueError(f"{name} must be on the GPU or in pinned host memory")
+    if t.shape[2] != BLOCK_SIZE:
+        raise ValueError(f"{name}: block size must be {BLOCK_SIZE}")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
+    return t.shape[1], t.shape[3]
+
+
+def copy_blocks(k_cache, v_cache, src_blocks, dst_blocks):
+    """Copy-on-write block copies inside one pool pair (pa_copy_blocks)."""
+    prepare_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks)()
+
+
+def prepare_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks):
+    nb, hkv, bs, d = _cache_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _check(src_blocks, "src_blocks", torch.int32, 1, dev)
+    _check(dst_blocks, "dst_blocks", torch.int32, 1, dev)
+    n = src_blocks.shape[0]
+    if dst_blocks.shape[0] != n:
+        raise ValueError("src_blocks and dst_blocks must have the same length")
+    return Call("pa_copy_blocks", (_ptr(k_cache), _ptr(v_cache), _ptr(src_blocks), _ptr(dst_blocks),
+                                   n, hkv, d, bs, nb, _stream(dev)),
+                keep=(k_cache, v_cache, src_blocks, dst_blocks))
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, src_blocks, dst_blocks):
+    """Block moves between two pool pairs (pa_swap_blocks); either side may be
+    pinned host memory (swap-out / swap-in over PCIe).  The id lists live on the GPU."""
+    prepare_swap_blocks(dst_k, dst_v, src_k, src_v, src_blocks, dst_blocks)()
+
+
+def prepare_swap_blocks(dst_k, dst_v, src_k, src_v, src_blocks, dst_blocks):
+    dims = {_pool_dims(t, n) for t, n in ((dst_k, "dst_k"), (dst_v, "dst_v"), (src_k, "src_k"),
+                                          (src_v, "src_v"))}
+    if len(dims) != 1:
+        raise ValueError("all four pools must share Hkv and head_dim")
+    (hkv, d), = dims
+    if src_blocks.device.type != "cuda":
+        raise ValueError("src_blocks/dst_blocks must be on the GPU")
+    dev = src_blocks.device
+    _check(src_blocks, "src_blocks", torch.int32, 1, dev)
+    _check(dst_blocks, "dst_blocks", torch.int32, 1, dev)
+    n = src_blocks.shape[0]
+    if dst_blocks.shape[0] != n:
+        raise ValueError("src_blocks and dst_blocks must have the same length")
+    return Call("pa_swap_blocks", (_ptr(dst_k), _ptr(dst_v), _ptr(src_k), _ptr(src_v),
+                                   _ptr(src_blocks), _ptr(dst_blocks), n, hkv, d, BLOCK_SIZE,
+                                   _stream(dev)),
+                keep=(dst_k, dst_v, src_k, src_v, src_blocks, dst_blocks))
 
 
 def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,

@@ -61,6 +61,20 @@ pa_status check_decode(const void* q, const void* k_cache, const void* v_cache,
   return PA_OK;
 }
 
+// True when the device can read and write p directly: device memory, or
+// pinned host memory mapped for the device.  Pageable host memory (which a
+// kernel cannot touch) and unknown pointers are refused; a failed query's
+// error state is cleared so it cannot surface in a later launch check.
+bool device_accessible(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (a.type == hipMemoryTypeDevice) return true;
+  return a.type == hipMemoryTypeHost && a.devicePointer != nullptr;
+}
+
 int32_t resolve_partition(int32_t partition_size, int32_t B, int32_t Hkv, int32_t max_context_len) {
   return partition_size == -1 ? pa_decode_partition_size(B, Hkv, max_context_len) : partition_size;
 }
@@ -77,6 +91,7 @@ const char* pa_status_str(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape not implemented (block_size 16, head_dim 64/128, Hq/Hkv <= 8)";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error";
+    case PA_ERR_MEMORY: return "PA_ERR_MEMORY: a pointer is neither device memory nor device-accessible pinned host memory";
   }
   return "unknown pa_status";
 }
@@ -220,6 +235,32 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
   // rows of sequence b are its NQ * Hq (query, head) pairs
   return from_hip(pa::launch_decode_combine(out, o_part, lse, context_lens, B, NQ * Hq, D, (int)np,
                                             P, s));
+}
+
+pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                         const int32_t* src_blocks, const int32_t* dst_blocks, int32_t n,
+                         int32_t Hkv, int32_t D, int32_t block_size, pa_stream_t stream) {
+  if (!dst_k || !dst_v || !src_k || !src_v) return PA_ERR_NULL;
+  if (n < 0 || Hkv <= 0 || D <= 0) return PA_ERR_SHAPE;
+  if (D != 64 && D != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != pa::kBlockSizeHost) return block_size > 0 ? PA_ERR_UNSUPPORTED : PA_ERR_SHAPE;
+  if (n == 0) return PA_OK;  // the id lists may then be NULL
+  if (!src_blocks || !dst_blocks) return PA_ERR_NULL;
+  const void* ptrs[6] = {dst_k, dst_v, src_k, src_v, src_blocks, dst_blocks};
+  for (const void* p : ptrs)
+    if (!device_accessible(p)) return PA_ERR_MEMORY;
+  const int64_t bytes = (int64_t)Hkv * block_size * D * 2;
+  return from_hip(pa::launch_block_copy(dst_k, dst_v, src_k, src_v, src_blocks, dst_blocks, n,
+                                        bytes, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks,
+                         const int32_t* dst_blocks, int32_t n, int32_t Hkv, int32_t D,
+                         int32_t block_size, int64_t num_blocks, pa_stream_t stream) {
+  if (!k_cache || !v_cache) return PA_ERR_NULL;
+  if (num_blocks < 0 || (n > 0 && num_blocks == 0)) return PA_ERR_SHAPE;
+  return pa_swap_blocks(k_cache, v_cache, k_cache, v_cache, src_blocks, dst_blocks, n, Hkv, D,
+                        block_size, stream);
 }
 
 pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,

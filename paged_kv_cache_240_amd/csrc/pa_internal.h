@@ -34,6 +34,11 @@ hipError_t launch_decode_combine(void* out, const float* o_part, const float* ls
                                  const int32_t* context_lens, int B, int Hq, int D,
                                  int num_partitions, int partition_size, hipStream_t stream);
 
+// Whole-block copies src pools -> dst pools for n (src, dst) id pairs.
+hipError_t launch_block_copy(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                             const int32_t* src_ids, const int32_t* dst_ids, int n,
+                             int64_t bytes_per_block, hipStream_t stream);
+
 hipError_t launch_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, const int32_t* context_lens,
                           const int32_t* query_start_loc, int B, int Hq, int Hkv, int D,

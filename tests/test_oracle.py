@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle
+import workloads as W
 from workloads import as_bits, from_bits, rope_cos_sin_table
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -520,3 +521,59 @@ def test_rope_rounds_each_fp32_operation():
     got = oracle.rope_rotate_half(x, cc, ss)
     assert np.array_equal(got[:, 0], bf(step_lo[cand]))
     assert np.array_equal(got[:, D // 2], bf(step_hi[cand]))
+
+
+# --------------------------------------------------------------------------
+# Block copies (copy-on-write, swap)
+# --------------------------------------------------------------------------
+
+def _pool(nb, seed, hkv=2, d=8):
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 2 ** 16, size=(nb, hkv, 16, d), dtype=np.uint16)
+
+
+def test_copy_blocks_equals_index_copy():
+    src, dst = _pool(10, 1), _pool(12, 2)
+    s_ids = np.array([3, 0, 9, 3], dtype=np.int32)
+    d_ids = np.array([11, 2, 5, 7], dtype=np.int32)
+    got = oracle.copy_blocks(dst, src, s_ids, d_ids)
+    want = torch.from_numpy(dst.astype(np.int32)).index_copy(
+        0, torch.from_numpy(d_ids.astype(np.int64)),
+        torch.from_numpy(src[s_ids].astype(np.int32))).numpy().astype(np.uint16)
+    assert np.array_equal(got, want)
+    untouched = np.setdiff1d(np.arange(12), d_ids)
+    assert np.array_equal(got[untouched], dst[untouched])
+
+
+def test_copy_within_one_pool_reads_the_old_tiles():
+    pool = _pool(6, 3)
+    got = oracle.copy_blocks(pool, pool, [1, 2], [4, 5])
+    assert np.array_equal(got[4], pool[1]) and np.array_equal(got[5], pool[2])
+    assert np.array_equal(got[:4], pool[:4])
+
+
+def test_swap_out_then_in_restores_the_sequence():
+    dev = _pool(16, 4)
+    seq_blocks = np.array([7, 2, 11], dtype=np.int32)
+    host = np.zeros((4, 2, 16, 8), dtype=np.uint16)
+    host = oracle.copy_blocks(host, dev, seq_blocks, [0, 1, 2])        # swap out
+    new_blocks = np.array([5, 13, 0], dtype=np.int32)
+    back = oracle.copy_blocks(np.zeros_like(dev), host, [0, 1, 2], new_blocks)  # swap in elsewhere
+    assert np.array_equal(back[new_blocks], dev[seq_blocks])
+
+
+def test_copy_on_write_then_decode_is_unchanged():
+    # a shared prefix block copied to a fresh block: the sequence that now points at the
+    # copy attends to exactly the same keys and values (aliasing vs private copy)
+    b = W.decode_batch([40, 40], 4, 2, 64, 16, 77, shared_prefix=([0, 1], 2))
+    qb, kc, vc = as_bits(b.q), as_bits(b.k_cache), as_bits(b.v_cache)
+    bt = b.block_tables.numpy().copy()
+    lens = b.context_lens.numpy()
+    ref = oracle.decode(qb, kc, vc, bt, lens, b.scale)
+    assert bt[0, 0] == bt[1, 0] and bt[0, 1] == bt[1, 1]  # shared blocks
+    free = np.setdiff1d(np.arange(16), bt[bt >= 0])[:2]
+    kc2 = oracle.copy_blocks(kc, kc, bt[1, :2], free)
+    vc2 = oracle.copy_blocks(vc, vc, bt[1, :2], free)
+    bt[1, :2] = free
+    got = oracle.decode(qb, kc2, vc2, bt, lens, b.scale)
+    assert np.array_equal(got, ref)
