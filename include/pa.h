@@ -58,7 +58,8 @@ typedef enum {
   PA_ERR_UNSUPPORTED = 3,  /* consistent, but a shape this library does not implement */
   PA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required */
   PA_ERR_HIP = 5,          /* the HIP runtime reported an error while enqueueing */
-  PA_ERR_MEMORY = 6        /* a pool is neither device memory nor device-accessible pinned host memory */
+  PA_ERR_MEMORY = 6,       /* a pool is neither device memory nor device-accessible pinned host memory */
+  PA_ERR_CAPACITY = 7      /* block manager: not enough free blocks (or output space); nothing changed */
 } pa_status;
 
 /* Static, human-readable name of a status code.  Never NULL. */
@@ -263,6 +264,81 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks
 pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
                          const int32_t* src_blocks, const int32_t* dst_blocks, int32_t n,
                          int32_t Hkv, int32_t D, int32_t block_size, pa_stream_t stream);
+
+/*
+ * Host block manager ([mini-llm] §3.1 physical blocks with ref counts, O(1)
+ * free list, per-sequence logical->physical table; §3.4 full blocks shared by
+ * content hash, copy-on-write; §3.5 swap-out / swap-in; [Pico-vLLM] §3 LRU
+ * eviction of cached blocks with lazy deletion).  Host memory only; it
+ * produces the block tables and slot mappings the kernels consume and the
+ * block pairs pa_copy_blocks / pa_swap_blocks move.  Not thread-safe: one
+ * caller at a time per manager.  Block size 16.
+ *
+ * Policy: a full block's hash chains the previous block's hash with its 16
+ * tokens (a hit is confirmed by comparing the tokens); hashes are registered
+ * by pa_bm_commit once the tokens' K/V are written; prefix reuse stops at the
+ * first miss and always leaves at least one prompt token to compute; a
+ * released hashed block stays cached (evictable) until an allocation finds no
+ * never-cached free block, then the least recently released one is reused.
+ * Errors leave the manager unchanged.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* NULL on invalid sizes (num_blocks <= 0, num_host_blocks < 0, block_size != 16)
+   or when out of host memory. */
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t num_host_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* m);
+
+/* Free + evictable cached blocks; cached (released, hashed) blocks; free host slots;
+   a block's ref count (-1 for a bad id). */
+int32_t pa_bm_num_free_blocks(const pa_block_manager* m);
+int32_t pa_bm_num_cached_blocks(const pa_block_manager* m);
+int32_t pa_bm_num_free_host_blocks(const pa_block_manager* m);
+int32_t pa_bm_block_ref(const pa_block_manager* m, int32_t block);
+
+/* New sequence with a prompt of n_tokens token ids (host array).  Reuses cached
+   blocks of the longest identical full-block prefix (ref_count + 1) and allocates
+   the rest; *n_cached_tokens = prompt tokens whose K/V are already in the cache
+   (a multiple of 16, < n_tokens).  PA_ERR_CAPACITY if blocks run out. */
+pa_status pa_bm_add_sequence(pa_block_manager* m, int64_t seq_id, const int32_t* tokens,
+                             int32_t n_tokens, int32_t* n_cached_tokens);
+
+/* The first n_computed_tokens of the sequence have their K/V written: register the
+   hashes of its full blocks in that range (first writer of a content wins). */
+pa_status pa_bm_commit(pa_block_manager* m, int64_t seq_id, int32_t n_computed_tokens);
+
+/* Reserve the slot of the sequence's next token (decode): a new block when the last
+   is full; if the last block is shared (after pa_bm_fork), the sequence first moves
+   to a fresh block and *cow_src / *cow_dst name the copy to run (else both -1). */
+pa_status pa_bm_append_token(pa_block_manager* m, int64_t seq_id, int32_t token, int32_t* slot,
+                             int32_t* cow_src, int32_t* cow_dst);
+
+/* Child shares every block of the parent (ref_count + 1 each). */
+pa_status pa_bm_fork(pa_block_manager* m, int64_t parent_id, int64_t child_id);
+
+/* Release every block (or host slot) of the sequence. */
+pa_status pa_bm_free_sequence(pa_block_manager* m, int64_t seq_id);
+
+/* Tokens held by the sequence (-1 if unknown). */
+int32_t pa_bm_seq_len(const pa_block_manager* m, int64_t seq_id);
+
+/* The sequence's block table into out[capacity]; *n_blocks = its length (set even
+   when capacity is too small, which returns PA_ERR_CAPACITY). */
+pa_status pa_bm_block_table(const pa_block_manager* m, int64_t seq_id, int32_t* out,
+                            int32_t capacity, int32_t* n_blocks);
+
+/* slot_mapping[i] = slot of token start + i, i < n (tokens must be reserved). */
+pa_status pa_bm_slots(const pa_block_manager* m, int64_t seq_id, int32_t start, int32_t n,
+                      int32_t* slot_mapping);
+
+/* Swap-out: the sequence's device blocks get host slots (pairs written to
+   device_blocks[i] -> host_blocks[i], *n of them) and are released.  Swap-in:
+   new device blocks for its host slots (host_blocks[i] -> device_blocks[i]);
+   the slots are released.  Run the pairs with pa_swap_blocks. */
+pa_status pa_bm_swap_out(pa_block_manager* m, int64_t seq_id, int32_t* device_blocks,
+                         int32_t* host_blocks, int32_t capacity, int32_t* n);
+pa_status pa_bm_swap_in(pa_block_manager* m, int64_t seq_id, int32_t* host_blocks,
+                        int32_t* device_blocks, int32_t capacity, int32_t* n);
 
 #ifdef __cplusplus
 }

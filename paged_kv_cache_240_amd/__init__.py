@@ -24,14 +24,14 @@ __all__ = ["load", "PAError", "Call", "cache_store", "decode", "decode_partition
            "prepare_decode_partitions", "prepare_decode_combine", "prepare_prefill",
            "decode_workspace_bytes", "decode_partition_size", "decode_multi", "prepare_decode_multi",
            "decode_multi_workspace_bytes", "copy_blocks", "swap_blocks", "prepare_copy_blocks",
-           "prepare_swap_blocks", "BLOCK_SIZE", "library_path",
+           "prepare_swap_blocks", "BlockManager", "BLOCK_SIZE", "library_path",
            "STATUS"]
 
 BLOCK_SIZE = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpa.so")
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
-          4: "PA_ERR_WORKSPACE", 5: "PA_ERR_HIP", 6: "PA_ERR_MEMORY"}
+          4: "PA_ERR_WORKSPACE", 5: "PA_ERR_HIP", 6: "PA_ERR_MEMORY", 7: "PA_ERR_CAPACITY"}
 
 _lib = None
 
@@ -56,6 +56,22 @@ _SIGS = {
                                   _i32, _i32, _f32, _p]),
     "pa_decode_multi_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_copy_blocks": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _p]),
+    "pa_bm_create": (_p, [_i32, _i32, _i32]),
+    "pa_bm_destroy": (None, [_p]),
+    "pa_bm_num_free_blocks": (_i32, [_p]),
+    "pa_bm_num_cached_blocks": (_i32, [_p]),
+    "pa_bm_num_free_host_blocks": (_i32, [_p]),
+    "pa_bm_block_ref": (_i32, [_p, _i32]),
+    "pa_bm_add_sequence": (ctypes.c_int, [_p, _i64, _p, _i32, _p]),
+    "pa_bm_commit": (ctypes.c_int, [_p, _i64, _i32]),
+    "pa_bm_append_token": (ctypes.c_int, [_p, _i64, _i32, _p, _p, _p]),
+    "pa_bm_fork": (ctypes.c_int, [_p, _i64, _i64]),
+    "pa_bm_free_sequence": (ctypes.c_int, [_p, _i64]),
+    "pa_bm_seq_len": (_i32, [_p, _i64]),
+    "pa_bm_block_table": (ctypes.c_int, [_p, _i64, _p, _i32, _p]),
+    "pa_bm_slots": (ctypes.c_int, [_p, _i64, _i32, _i32, _p]),
+    "pa_bm_swap_out": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p]),
+    "pa_bm_swap_in": (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p]),
     "pa_swap_blocks": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
     "pa_decode_multi": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _i32, _f32, _i32, _p, _sz, _p]),
@@ -431,3 +447,104 @@ def prepare_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start
                                block_tables.shape[1], int(max_query_len), float(scale),
                                _stream(dev)),
                 result=out, keep=(q, k_cache, v_cache, block_tables, context_lens, query_start_loc))
+
+
+class BlockManager:
+    """The C++ host block manager of libpa (pa_bm_*): block tables, slot mappings,
+    prefix reuse by content, copy-on-write after fork, swap bookkeeping."""
+
+    def __init__(self, num_blocks, num_host_blocks=0, block_size=BLOCK_SIZE):
+        self._lib = load()
+        self._h = self._lib.pa_bm_create(int(num_blocks), int(num_host_blocks), int(block_size))
+        if not self._h:
+            raise ValueError("pa_bm_create: bad sizes (block_size must be 16)")
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def _ok(self, name, st):
+        if st != 0:
+            raise PAError(name, st)
+
+    @property
+    def num_free_blocks(self):
+        return int(self._lib.pa_bm_num_free_blocks(self._h))
+
+    @property
+    def num_cached_blocks(self):
+        return int(self._lib.pa_bm_num_cached_blocks(self._h))
+
+    @property
+    def num_free_host_blocks(self):
+        return int(self._lib.pa_bm_num_free_host_blocks(self._h))
+
+    def block_ref(self, block):
+        return int(self._lib.pa_bm_block_ref(self._h, int(block)))
+
+    def add_sequence(self, seq_id, tokens):
+        """Returns the number of prompt tokens already cached (reused blocks)."""
+        arr = (ctypes.c_int32 * len(tokens))(*[int(t) for t in tokens])
+        n = ctypes.c_int32()
+        self._ok("pa_bm_add_sequence", self._lib.pa_bm_add_sequence(
+            self._h, int(seq_id), arr, len(tokens), ctypes.byref(n)))
+        return n.value
+
+    def commit(self, seq_id, n_computed_tokens):
+        self._ok("pa_bm_commit", self._lib.pa_bm_commit(self._h, int(seq_id), int(n_computed_tokens)))
+
+    def append_token(self, seq_id, token):
+        """Returns (slot, cow) with cow = (src_block, dst_block) or None."""
+        slot, src, dst = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        self._ok("pa_bm_append_token", self._lib.pa_bm_append_token(
+            self._h, int(seq_id), int(token), ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst)))
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def fork(self, parent_id, child_id):
+        self._ok("pa_bm_fork", self._lib.pa_bm_fork(self._h, int(parent_id), int(child_id)))
+
+    def free_sequence(self, seq_id):
+        self._ok("pa_bm_free_sequence", self._lib.pa_bm_free_sequence(self._h, int(seq_id)))
+
+    def seq_len(self, seq_id):
+        return int(self._lib.pa_bm_seq_len(self._h, int(seq_id)))
+
+    def block_table(self, seq_id):
+        n = ctypes.c_int32()
+        st = self._lib.pa_bm_block_table(self._h, int(seq_id), None, 0, ctypes.byref(n))
+        if st not in (0, 7):
+            raise PAError("pa_bm_block_table", st)
+        out = (ctypes.c_int32 * max(1, n.value))()
+        self._ok("pa_bm_block_table", self._lib.pa_bm_block_table(
+            self._h, int(seq_id), out, n.value, ctypes.byref(n)))
+        return list(out[:n.value])
+
+    def slots(self, seq_id, start, n):
+        out = (ctypes.c_int32 * max(1, n))()
+        self._ok("pa_bm_slots", self._lib.pa_bm_slots(self._h, int(seq_id), int(start), int(n), out))
+        return list(out[:n])
+
+    def _swap(self, fn, seq_id):
+        cap = max(1, len(self.block_table(seq_id)) if fn == "pa_bm_swap_out" else 4096)
+        while True:
+            a, b = (ctypes.c_int32 * cap)(), (ctypes.c_int32 * cap)()
+            n = ctypes.c_int32()
+            st = getattr(self._lib, fn)(self._h, int(seq_id), a, b, cap, ctypes.byref(n))
+            if st == 7 and n.value > cap:
+                cap = n.value
+                continue
+            self._ok(fn, st)
+            return list(a[:n.value]), list(b[:n.value])
+
+    def swap_out(self, seq_id):
+        """Returns (device_blocks, host_blocks): copy device -> host with pa_swap_blocks."""
+        return self._swap("pa_bm_swap_out", seq_id)
+
+    def swap_in(self, seq_id):
+        """Returns (host_blocks, device_blocks): copy host -> device with pa_swap_blocks."""
+        return self._swap("pa_bm_swap_in", seq_id)
+

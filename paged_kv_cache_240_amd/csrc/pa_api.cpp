@@ -92,6 +92,7 @@ const char* pa_status_str(pa_status s) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error";
     case PA_ERR_MEMORY: return "PA_ERR_MEMORY: a pointer is neither device memory nor device-accessible pinned host memory";
+    case PA_ERR_CAPACITY: return "PA_ERR_CAPACITY: not enough free blocks or output space";
   }
   return "unknown pa_status";
 }
