@@ -266,6 +266,27 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void
                          int32_t Hkv, int32_t D, int32_t block_size, pa_stream_t stream);
 
 /*
+ * Fused RMSNorm + residual add ([Pico-vLLM] §2 kernel layer; Qwen2.5's
+ * RMSNorm), per row t of H values:
+ *   r'        = bf16(x[t] + residual[t])   written back over residual[t]
+ *   out[t][j] = bf16(weight[j] * r'[j] / sqrt(mean_j(r'[j]^2) + eps))
+ * in fp32 with one final rounding (nearest even).  residual NULL: plain
+ * RMSNorm of x (r' = x, nothing written back).
+ * out, x, residual bf16 [T][H]; weight bf16 [H]; H a multiple of 8, at most
+ * 16384, else PA_ERR_UNSUPPORTED.  out may alias neither x nor residual.
+ */
+pa_status pa_rmsnorm_residual(void* out, void* residual, const void* x, const void* weight,
+                              int32_t T, int32_t H, float eps, pa_stream_t stream);
+
+/*
+ * Fused SwiGLU ([Pico-vLLM] §2 kernel layer; Qwen2.5's MLP activation), per
+ * row t: gate = gate_up[t][0 .. I), up = gate_up[t][I .. 2I),
+ *   out[t][j] = bf16(gate[j] / (1 + e^(-gate[j])) * up[j])   (fp32, nearest even).
+ * out bf16 [T][I]; gate_up bf16 [T][2I]; I a multiple of 8.
+ */
+pa_status pa_swiglu(void* out, const void* gate_up, int64_t T, int32_t I, pa_stream_t stream);
+
+/*
  * Host block manager ([mini-llm] §3.1 physical blocks with ref counts, O(1)
  * free list, per-sequence logical->physical table; §3.4 full blocks shared by
  * content hash, copy-on-write; §3.5 swap-out / swap-in; [Pico-vLLM] §3 LRU

@@ -28,13 +28,15 @@ Modules:
              combine, and causal chunked prefill (multi-query verification is
              the chunked prefill with chunks of NQ rows).
   blocks     whole-block copies between pools (copy-on-write, swap).
+  block_manager  plain-Python model of the host block manager's policy.
+  layer_ops  fused residual add + RMSNorm and fused SwiGLU.
 
 Every function here is pinned by ``tests/test_oracle.py`` against something
 other than itself (closed forms, library routines, invariants, brute force).
 No function of this package is "parity unpinned".
 """
 
-from . import bf16, store, attention, blocks  # noqa: F401
+from . import bf16, store, attention, blocks, layer_ops  # noqa: F401
 from .bf16 import (  # noqa: F401
     bf16_to_f32,
     bf16_to_f64,
@@ -53,3 +55,4 @@ from .attention import (  # noqa: F401
     prefill,
 )
 from .blocks import copy_blocks  # noqa: F401
+from .layer_ops import rmsnorm_residual, swiglu  # noqa: F401

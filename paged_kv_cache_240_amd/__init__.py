@@ -24,7 +24,8 @@ __all__ = ["load", "PAError", "Call", "cache_store", "decode", "decode_partition
            "prepare_decode_partitions", "prepare_decode_combine", "prepare_prefill",
            "decode_workspace_bytes", "decode_partition_size", "decode_multi", "prepare_decode_multi",
            "decode_multi_workspace_bytes", "copy_blocks", "swap_blocks", "prepare_copy_blocks",
-           "prepare_swap_blocks", "BlockManager", "BLOCK_SIZE", "library_path",
+           "prepare_swap_blocks", "BlockManager", "rmsnorm_residual", "prepare_rmsnorm_residual",
+           "swiglu", "prepare_swiglu", "BLOCK_SIZE", "library_path",
            "STATUS"]
 
 BLOCK_SIZE = 16
@@ -56,6 +57,8 @@ _SIGS = {
                                   _i32, _i32, _f32, _p]),
     "pa_decode_multi_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_copy_blocks": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i64, _p]),
+    "pa_rmsnorm_residual": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _f32, _p]),
+    "pa_swiglu": (ctypes.c_int, [_p, _p, _i64, _i32, _p]),
     "pa_bm_create": (_p, [_i32, _i32, _i32]),
     "pa_bm_destroy": (None, [_p]),
     "pa_bm_num_free_blocks": (_i32, [_p]),
@@ -447,6 +450,49 @@ def prepare_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start
                                block_tables.shape[1], int(max_query_len), float(scale),
                                _stream(dev)),
                 result=out, keep=(q, k_cache, v_cache, block_tables, context_lens, query_start_loc))
+
+
+def rmsnorm_residual(x, weight, residual=None, eps=1e-6, out=None):
+    """Fused residual add + RMSNorm (pa_rmsnorm_residual).  x, residual bf16 [T, H]
+    (residual updated in place to x + residual); weight bf16 [H].  Returns out."""
+    return prepare_rmsnorm_residual(x, weight, residual, eps, out)()
+
+
+def prepare_rmsnorm_residual(x, weight, residual=None, eps=1e-6, out=None):
+    dev = x.device
+    _check(x, "x", torch.bfloat16, 2, dev)
+    T, H = x.shape
+    _check(weight, "weight", torch.bfloat16, 1, dev)
+    if weight.shape[0] != H:
+        raise ValueError("weight must have H entries")
+    if residual is not None:
+        _check(residual, "residual", torch.bfloat16, 2, dev)
+        if residual.shape != x.shape:
+            raise ValueError("residual must have x's shape")
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", torch.bfloat16, 2, dev)
+    return Call("pa_rmsnorm_residual", (_ptr(out), _ptr(residual), _ptr(x), _ptr(weight), T, H,
+                                        float(eps), _stream(dev)),
+                result=out, keep=(x, weight, residual, out))
+
+
+def swiglu(gate_up, out=None):
+    """Fused SwiGLU (pa_swiglu): gate_up bf16 [T, 2I] -> silu(gate) * up, bf16 [T, I]."""
+    return prepare_swiglu(gate_up, out)()
+
+
+def prepare_swiglu(gate_up, out=None):
+    dev = gate_up.device
+    _check(gate_up, "gate_up", torch.bfloat16, 2, dev)
+    T, I2 = gate_up.shape
+    if I2 % 2:
+        raise ValueError("gate_up must hold gate and up halves")
+    if out is None:
+        out = torch.empty((T, I2 // 2), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, 2, dev)
+    return Call("pa_swiglu", (_ptr(out), _ptr(gate_up), T, I2 // 2, _stream(dev)), result=out,
+                keep=(gate_up, out))
 
 
 class BlockManager:

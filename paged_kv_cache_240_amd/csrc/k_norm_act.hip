@@ -1,0 +1,137 @@
+// Fused RMSNorm + residual add and fused SwiGLU for gfx950: the elementwise
+// neighbours of attention in a decoder layer (Pico-vLLM write-up, §2 kernel
+// layer: RMSNorm fused with the residual add; SwiGLU fused).
+//
+// rmsnorm_residual, one row of H values per workgroup:
+//   r'  = bf16(x + r)                          (written back over r; exact in fp32)
+//   out = bf16(w * r' / sqrt(mean(r'^2) + eps)) (fp32, one rounding)
+// With no residual, r' = x and nothing is written back.
+// swiglu, per element of a row of 2I values [gate | up]:
+//   out = bf16(silu(gate) * up),  silu(g) = g / (1 + e^-g)   (fp32)
+//
+// Both read every input once and write every output once with 16-byte
+// accesses: HBM-bound.
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kNormThreads = 256;
+
+__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
+  f[0] = bf16lo(v.x); f[1] = bf16hi(v.x); f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
+  f[4] = bf16lo(v.z); f[5] = bf16hi(v.z); f[6] = bf16lo(v.w); f[7] = bf16hi(v.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+// A row's pieces stay in registers between the sum of squares and the scaling:
+// PER = pieces of 8 values per thread (H <= 8 * PER * kNormThreads).
+template <int PER, bool RESID>
+__global__ void __launch_bounds__(kNormThreads)
+rmsnorm_kernel(uint16_t* __restrict__ out, uint16_t* __restrict__ residual,
+               const uint16_t* __restrict__ x, const uint16_t* __restrict__ weight, int H,
+               float eps) {
+  __shared__ float part[kNormThreads / 64];
+  const int row = blockIdx.x;
+  const int n8 = H / 8;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (int64_t)row * H);
+  uint4* rr = reinterpret_cast<uint4*>(residual + (int64_t)row * H);
+  float v[PER][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = threadIdx.x + k * kNormThreads;
+    if (i < n8) {
+      unpack8(xr[i], v[k]);
+      if (RESID) {
+        float r[8];
+        unpack8(rr[i], r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[k][e] = bf16lo(f32_to_bf16_rne(v[k][e] + r[e]));
+        rr[i] = pack8(v[k]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(v[k][e], v[k][e], ss);
+    }
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kNormThreads / 64; ++w) tot += part[w];
+  const float inv = 1.f / sqrtf(tot / (float)H + eps);
+  const uint4* wr = reinterpret_cast<const uint4*>(weight);
+  uint4* orow = reinterpret_cast<uint4*>(out + (int64_t)row * H);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = threadIdx.x + k * kNormThreads;
+    if (i < n8) {
+      float w[8];
+      unpack8(wr[i], w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = w[e] * (v[k][e] * inv);
+      orow[i] = pack8(w);
+    }
+  }
+}
+
+// Grid-stride over 8-value pieces of the output [T][I].
+__global__ void __launch_bounds__(256)
+swiglu_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ gate_up, int64_t T, int I) {
+  const int n8 = I / 8;
+  const int64_t total = T * n8;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
+       p += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = p / n8;
+    const int c = (int)(p % n8);
+    const uint4* row = reinterpret_cast<const uint4*>(gate_up + t * 2 * I);
+    float g[8], u[8], y[8];
+    unpack8(load_stream16(row + c), g);
+    unpack8(load_stream16(row + n8 + c), u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = g[e] / (1.f + expf(-g[e])) * u[e];
+    reinterpret_cast<uint4*>(out + t * I)[c] = pack8(y);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(void* out, void* residual, const void* x, const void* weight, int T,
+                          int H, float eps, hipStream_t stream) {
+  const int n8 = H / 8;
+  auto* o = static_cast<uint16_t*>(out);
+  auto* r = static_cast<uint16_t*>(residual);
+  const auto* xx = static_cast<const uint16_t*>(x);
+  const auto* w = static_cast<const uint16_t*>(weight);
+#define PA_NORM(PER)                                                                          \
+  do {                                                                                        \
+    if (r) hipLaunchKernelGGL((rmsnorm_kernel<PER, true>), dim3(T), dim3(kNormThreads), 0,   \
+                              stream, o, r, xx, w, H, eps);                                   \
+    else hipLaunchKernelGGL((rmsnorm_kernel<PER, false>), dim3(T), dim3(kNormThreads), 0,    \
+                            stream, o, r, xx, w, H, eps);                                     \
+  } while (0)
+  if (n8 <= kNormThreads) PA_NORM(1);
+  else if (n8 <= 2 * kNormThreads) PA_NORM(2);
+  else if (n8 <= 4 * kNormThreads) PA_NORM(4);
+  else PA_NORM(8);
+#undef PA_NORM
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(void* out, const void* gate_up, int64_t T, int I, hipStream_t stream) {
+  const int64_t pieces = T * (I / 8);
+  const int64_t want = (pieces + 255) / 256;
+  const int grid = (int)(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(swiglu_kernel, dim3(grid), dim3(256), 0, stream, static_cast<uint16_t*>(out),
+                     static_cast<const uint16_t*>(gate_up), T, I);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -264,6 +264,24 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks
                         block_size, stream);
 }
 
+pa_status pa_rmsnorm_residual(void* out, void* residual, const void* x, const void* weight,
+                              int32_t T, int32_t H, float eps, pa_stream_t stream) {
+  if (!out || !x || !weight) return PA_ERR_NULL;
+  if (T < 0 || H <= 0 || !(eps >= 0.f)) return PA_ERR_SHAPE;
+  if (H % 8 != 0 || H > 16384) return PA_ERR_UNSUPPORTED;
+  if (T == 0) return PA_OK;
+  return from_hip(pa::launch_rmsnorm(out, residual, x, weight, T, H, eps,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_swiglu(void* out, const void* gate_up, int64_t T, int32_t I, pa_stream_t stream) {
+  if (!out || !gate_up) return PA_ERR_NULL;
+  if (T < 0 || I <= 0) return PA_ERR_SHAPE;
+  if (I % 8 != 0) return PA_ERR_UNSUPPORTED;
+  if (T == 0) return PA_OK;
+  return from_hip(pa::launch_swiglu(out, gate_up, T, I, static_cast<hipStream_t>(stream)));
+}
+
 pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, const int32_t* context_lens,
                      const int32_t* query_start_loc, int32_t B, int32_t T, int32_t Hq, int32_t Hkv,

@@ -39,6 +39,11 @@ hipError_t launch_block_copy(void* dst_k, void* dst_v, const void* src_k, const 
                              const int32_t* src_ids, const int32_t* dst_ids, int n,
                              int64_t bytes_per_block, hipStream_t stream);
 
+hipError_t launch_rmsnorm(void* out, void* residual, const void* x, const void* weight, int T,
+                          int H, float eps, hipStream_t stream);
+
+hipError_t launch_swiglu(void* out, const void* gate_up, int64_t T, int I, hipStream_t stream);
+
 hipError_t launch_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, const int32_t* context_lens,
                           const int32_t* query_start_loc, int B, int Hq, int Hkv, int D,

@@ -191,3 +191,22 @@ def _swap(**kw):
 ])
 def test_swap_blocks_validation(kw, code):
     assert _swap(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, None, P, P, 4, 64, 1e-6), NULL), ((P, None, None, P, 4, 64, 1e-6), NULL),
+    ((P, None, P, None, 4, 64, 1e-6), NULL), ((P, None, P, P, -1, 64, 1e-6), SHAPE),
+    ((P, None, P, P, 4, 0, 1e-6), SHAPE), ((P, None, P, P, 4, 60, 1e-6), UNSUP),
+    ((P, None, P, P, 4, 16392, 1e-6), UNSUP), ((P, None, P, P, 4, 64, -1.0), SHAPE),
+    ((P, None, P, P, 4, 64, float("nan")), SHAPE), ((P, P, P, P, 0, 64, 1e-6), OK),
+])
+def test_rmsnorm_validation(args, code):
+    assert pa.load().pa_rmsnorm_residual(*args, None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, P, 4, 64), NULL), ((P, None, 4, 64), NULL), ((P, P, -1, 64), SHAPE),
+    ((P, P, 4, 0), SHAPE), ((P, P, 4, 12), UNSUP), ((P, P, 0, 64), OK),
+])
+def test_swiglu_validation(args, code):
+    assert pa.load().pa_swiglu(*args, None) == code

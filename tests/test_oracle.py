@@ -577,3 +577,57 @@ def test_copy_on_write_then_decode_is_unchanged():
     bt[1, :2] = free
     got = oracle.decode(qb, kc2, vc2, bt, lens, b.scale)
     assert np.array_equal(got, ref)
+
+
+# --------------------------------------------------------------------------
+# Residual add + RMSNorm, SwiGLU
+# --------------------------------------------------------------------------
+
+def _bf16_bits(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_rmsnorm_matches_torch_rms_norm():
+    rng = np.random.default_rng(5)
+    x = _bf16_bits(rng.standard_normal((6, 96)))
+    w = _bf16_bits(rng.standard_normal(96))
+    got, r = oracle.rmsnorm_residual(x, w, None, eps=1e-6)
+    xt = torch.from_numpy(oracle.bf16_to_f64(x))
+    want = torch.nn.functional.rms_norm(xt, (96,), torch.from_numpy(oracle.bf16_to_f64(w)), eps=1e-6)
+    assert r is None and np.allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_rmsnorm_closed_forms():
+    # constant row c: rms = |c|, out = w * sign(c); unit weight: the output's rms is 1 (eps 0)
+    c = _bf16_bits(np.full((1, 64), -2.5))
+    w = _bf16_bits(np.linspace(-1, 1, 64))
+    out, _ = oracle.rmsnorm_residual(c, w, None, eps=0.0)
+    assert np.allclose(out, -oracle.bf16_to_f64(w))
+    x = _bf16_bits(np.random.default_rng(6).standard_normal((3, 128)))
+    ones = _bf16_bits(np.ones(128))
+    out, _ = oracle.rmsnorm_residual(x, ones, None, eps=0.0)
+    assert np.allclose(np.sqrt((out ** 2).mean(-1)), 1.0, atol=1e-12)
+    # scale invariance: 4x has the same normalised output (4 is exact in bf16)
+    x4 = _bf16_bits(oracle.bf16_to_f64(x) * 4)
+    assert np.allclose(oracle.rmsnorm_residual(x4, ones, None, 0.0)[0], out, atol=1e-12)
+
+
+def test_residual_add_is_torch_bf16_addition():
+    rng = np.random.default_rng(7)
+    x = _bf16_bits(rng.standard_normal((5, 64)) * 3)
+    r = _bf16_bits(rng.standard_normal((5, 64)) * 1e-3)
+    _, nr = oracle.rmsnorm_residual(x, _bf16_bits(np.ones(64)), r)
+    tx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    tr = torch.from_numpy(r.view(np.int16)).view(torch.bfloat16)
+    assert np.array_equal(nr, (tx + tr).view(torch.int16).numpy().view(np.uint16))
+
+
+def test_swiglu_matches_torch_silu():
+    rng = np.random.default_rng(8)
+    gu = _bf16_bits(rng.standard_normal((4, 2 * 40)) * 4)
+    got = oracle.swiglu(gu)
+    t = torch.from_numpy(oracle.bf16_to_f64(gu))
+    want = torch.nn.functional.silu(t[:, :40]) * t[:, 40:]
+    assert np.allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)
+    z = oracle.swiglu(_bf16_bits(np.array([[0.0, 60.0, -60.0, 1.0, 2.0, 2.0]])))
+    assert z[0, 0] == 0.0 and abs(z[0, 1] - 2 * 60.0) < 1e-9 and abs(z[0, 2]) < 1e-20
