@@ -274,6 +274,29 @@ def run_blocks(device):
     return res
 
 
+def run_layer_ops(device):
+    """Fused RMSNorm + residual add and SwiGLU at the Qwen2.5-1.5B widths (hidden 1536,
+    intermediate 8960), for a prefill-sized batch of tokens and a decode-sized one.
+    Rates count bytes read plus bytes written once each."""
+    res = {}
+    g = torch.Generator().manual_seed(2413)
+    H, I = 1536, 8960
+    for T in (4096, 16):
+        x = torch.randn((T, H), generator=g).to(torch.bfloat16).to(device)
+        r = torch.randn((T, H), generator=g).to(torch.bfloat16).to(device)
+        w = torch.randn((H,), generator=g).to(torch.bfloat16).to(device)
+        norm = pa.prepare_rmsnorm_residual(x, w, r, eps=1e-6)
+        us = time_calls(norm, 200)
+        moved = 4 * T * H * 2 + H * 2          # x, r in; r', out out; the weight
+        res[f"rmsnorm_residual_T{T}_H{H}"] = {"us": round(us, 2), "GBps": round(moved / us / 1e3, 1)}
+        gu = torch.randn((T, 2 * I), generator=g).to(torch.bfloat16).to(device)
+        act = pa.prepare_swiglu(gu)
+        us = time_calls(act, 200)
+        moved = 3 * T * I * 2                  # gate and up in, the product out
+        res[f"swiglu_T{T}_I{I}"] = {"us": round(us, 2), "GBps": round(moved / us / 1e3, 1)}
+    return res
+
+
 def prefill_flops(b):
     """4 * D multiply-adds... per visible (row, key) pair: QK^T and PV, 2 flop each."""
     qsl = b.query_start_loc.cpu().numpy()
@@ -453,6 +476,7 @@ def main():
         line["context"] = run_context(dev)
         line["context"]["spec_verify_16x8192"] = run_verify(layers, args.steps, args.warmup)
         line["context"]["block_copies"] = run_blocks(dev)
+        line["context"]["layer_ops"] = run_layer_ops(dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layers, args.cpu_budget)
     else:

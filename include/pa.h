@@ -281,8 +281,12 @@ pa_status pa_rmsnorm_residual(void* out, void* residual, const void* x, const vo
 /*
  * Fused SwiGLU ([Pico-vLLM] §2 kernel layer; Qwen2.5's MLP activation), per
  * row t: gate = gate_up[t][0 .. I), up = gate_up[t][I .. 2I),
- *   out[t][j] = bf16(gate[j] / (1 + e^(-gate[j])) * up[j])   (fp32, nearest even).
- * out bf16 [T][I]; gate_up bf16 [T][2I]; I a multiple of 8.
+ *   out[t][j] = bf16(gate[j] / (1 + e^(-gate[j])) * up[j])
+ * in fp32 (hardware exp2 and reciprocal: a few fp32 ulps before the one
+ * rounding to bf16, nearest even); results down to the subnormals are kept
+ * for large negative gates.
+ * out bf16 [T][I]; gate_up bf16 [T][2I]; I a multiple of 8 and at most 2^26,
+ * T at most 2^31 - 1, else PA_ERR_UNSUPPORTED.
  */
 pa_status pa_swiglu(void* out, const void* gate_up, int64_t T, int32_t I, pa_stream_t stream);
 

@@ -32,4 +32,5 @@ def swiglu(gate_up_bits):
     gu = bf16_to_f64(gate_up_bits)
     i = gu.shape[-1] // 2
     g, u = gu[..., :i], gu[..., i:]
-    return g / (1.0 + np.exp(-g)) * u
+    with np.errstate(over="ignore"):   # e^-g = inf for very negative g: the quotient is then -0
+        return g / (1.0 + np.exp(-g)) * u

@@ -7,7 +7,7 @@
 //   out = bf16(w * r' / sqrt(mean(r'^2) + eps)) (fp32, one rounding)
 // With no residual, r' = x and nothing is written back.
 // swiglu, per element of a row of 2I values [gate | up]:
-//   out = bf16(silu(gate) * up),  silu(g) = g / (1 + e^-g)   (fp32)
+//   out = bf16(silu(gate) * up),  silu(g) = g / (1 + e^-g)   (fp32, see swiglu_piece)
 //
 // Both read every input once and write every output once with 16-byte
 // accesses: HBM-bound.
@@ -82,22 +82,71 @@ rmsnorm_kernel(uint16_t* __restrict__ out, uint16_t* __restrict__ residual,
   }
 }
 
-// Grid-stride over 8-value pieces of the output [T][I].
-__global__ void __launch_bounds__(256)
-swiglu_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ gate_up, int64_t T, int I) {
-  const int n8 = I / 8;
-  const int64_t total = T * n8;
-  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
-       p += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = p / n8;
-    const int c = (int)(p % n8);
-    const uint4* row = reinterpret_cast<const uint4*>(gate_up + t * 2 * I);
-    float g[8], u[8], y[8];
-    unpack8(load_stream16(row + c), g);
-    unpack8(load_stream16(row + n8 + c), u);
+constexpr int kActThreads = 256;
+constexpr int kActPieces = 2;  // 8-value pieces per thread: 4 loads of 16 B in flight
+
+// silu(g) * u = g * u * sigma(g), sigma(g) = 1 / (1 + 2^a), a = -g log2(e), from
+// v_exp_f32 and v_rcp_f32 (a few fp32 ulps, far below the final bf16 rounding).
+// Past a = 64 (g < -44.4) sigma(g) = 2^-a to within 2^-64 relative; there it is
+// applied as 2^-(a - n) times an exact scaling by 2^-n, so results that are
+// tiny but still representable (down to the subnormals) are not lost to an
+// overflow of 2^a.  That path is taken only when some value of the piece
+// needs it, so the common case runs without per-value branches.
+constexpr float kNegLog2e = -1.44269504088896341f;
+
+__device__ __forceinline__ uint4 swiglu_piece(const uint4 gw, const uint4 uw) {
+  float g[8], u[8], y[8], a[8];
+  unpack8(gw, g);
+  unpack8(uw, u);
+  float amax = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = g[e] / (1.f + expf(-g[e])) * u[e];
-    reinterpret_cast<uint4*>(out + t * I)[c] = pack8(y);
+  for (int e = 0; e < 8; ++e) {
+    a[e] = g[e] * kNegLog2e;
+    y[e] = g[e] * u[e] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(a[e]));
+    amax = fmaxf(amax, a[e]);
+  }
+  if (amax > 64.f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (a[e] > 64.f) {
+        const float n = fminf(__builtin_floorf(a[e]), 320.f);
+        y[e] = __builtin_amdgcn_ldexpf(g[e] * u[e] * __builtin_amdgcn_exp2f(n - a[e]), -(int)n);
+      }
+    }
+  }
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y[0], (__bf16)y[1]});
+  r.y = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y[2], (__bf16)y[3]});
+  r.z = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y[4], (__bf16)y[5]});
+  r.w = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y[6], (__bf16)y[7]});
+  return r;
+}
+
+// Row t = blockIdx.x; the row's I/8 pieces are cut into gridDim.y chunks of
+// `chunk` pieces, and thread i of a workgroup takes pieces i and i + 256 of
+// its chunk (no index division; all loads issued before any arithmetic).
+__global__ void __launch_bounds__(kActThreads)
+swiglu_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ gate_up, int I, int chunk) {
+  const int n8 = I / 8;
+  const int64_t t = blockIdx.x;
+  const uint4* grow = reinterpret_cast<const uint4*>(gate_up + t * 2 * I);
+  const uint4* urow = grow + n8;
+  uint4* orow = reinterpret_cast<uint4*>(out + t * I);
+  const int c0 = blockIdx.y * chunk;
+  const int c_end = min(c0 + chunk, n8);
+  uint4 g[kActPieces], u[kActPieces];
+#pragma unroll
+  for (int j = 0; j < kActPieces; ++j) {
+    const int c = c0 + j * kActThreads + (int)threadIdx.x;
+    if (c < c_end) {
+      g[j] = load_stream16(grow + c);
+      u[j] = load_stream16(urow + c);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kActPieces; ++j) {
+    const int c = c0 + j * kActThreads + (int)threadIdx.x;
+    if (c < c_end) orow[c] = swiglu_piece(g[j], u[j]);
   }
 }
 
@@ -126,11 +175,13 @@ hipError_t launch_rmsnorm(void* out, void* residual, const void* x, const void* 
 }
 
 hipError_t launch_swiglu(void* out, const void* gate_up, int64_t T, int I, hipStream_t stream) {
-  const int64_t pieces = T * (I / 8);
-  const int64_t want = (pieces + 255) / 256;
-  const int grid = (int)(want < 8192 ? want : 8192);
-  hipLaunchKernelGGL(swiglu_kernel, dim3(grid), dim3(256), 0, stream, static_cast<uint16_t*>(out),
-                     static_cast<const uint16_t*>(gate_up), T, I);
+  // balanced chunks of at most kActPieces * kActThreads pieces per row
+  const int n8 = I / 8;
+  const int per_wg = kActPieces * kActThreads;
+  const int chunks = (n8 + per_wg - 1) / per_wg;
+  const int chunk = (n8 + chunks - 1) / chunks;
+  hipLaunchKernelGGL(swiglu_kernel, dim3((uint32_t)T, chunks), dim3(kActThreads), 0, stream,
+                     static_cast<uint16_t*>(out), static_cast<const uint16_t*>(gate_up), I, chunk);
   return hipGetLastError();
 }
 

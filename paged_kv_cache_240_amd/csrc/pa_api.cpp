@@ -277,7 +277,7 @@ pa_status pa_rmsnorm_residual(void* out, void* residual, const void* x, const vo
 pa_status pa_swiglu(void* out, const void* gate_up, int64_t T, int32_t I, pa_stream_t stream) {
   if (!out || !gate_up) return PA_ERR_NULL;
   if (T < 0 || I <= 0) return PA_ERR_SHAPE;
-  if (I % 8 != 0) return PA_ERR_UNSUPPORTED;
+  if (I % 8 != 0 || I > (1 << 26) || T > INT32_MAX) return PA_ERR_UNSUPPORTED;
   if (T == 0) return PA_OK;
   return from_hip(pa::launch_swiglu(out, gate_up, T, I, static_cast<hipStream_t>(stream)));
 }

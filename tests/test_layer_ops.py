@@ -75,11 +75,16 @@ def test_swiglu(gpu, T, I):
 
 
 def test_swiglu_extremes(gpu):
-    vals = torch.tensor([0.0, 1.0, -1.0, 80.0, -80.0, 1e-30, -1e-30, 3.0e38], dtype=torch.float32)
-    gate = vals.repeat(2)[:8]
-    up = torch.tensor([1.0, 2.0, -2.0, 0.5, 7.0, 1.0, 1.0, 1e-37], dtype=torch.float32)
-    gu = torch.cat([gate, up]).view(1, 16).to(torch.bfloat16)
+    # zero, tiny and huge gates; large negative gates across the switch to the
+    # scaled form (near -44.4) and beyond the overflow of e^-g (below -88.7), whose
+    # results are tiny normals, then subnormals, then zero
+    gate = torch.tensor([0.0, 1.0, -1.0, 80.0, -80.0, 1e-30, -1e-30, 3.0e38,
+                         -44.0, -45.0, -60.0, -89.0, -95.0, -100.0, -120.0, -3.0e38], dtype=torch.float32)
+    up = torch.tensor([1.0, 2.0, -2.0, 0.5, 7.0, 1.0, 1.0, 1e-37,
+                       3.0, -3.0, 1.0, 1.0, 2.0, -1.0, 1.0, 1.0], dtype=torch.float32)
+    gu = torch.cat([gate, up]).view(1, 32).to(torch.bfloat16)
     want = oracle.swiglu(as_bits(gu))
+    assert want[0, 11] != 0 and abs(want[0, 11]) > 2.0 ** -126   # -89: a normal result
     out = gpu.swiglu(gu.cuda())
     torch.cuda.synchronize()
     _close(out, want, "extremes")
