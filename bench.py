@@ -6,21 +6,24 @@ Headline workload (the long-context flash-decode): 16 sequences x 8192 cached
 tokens, 12 query / 2 KV heads (the Qwen2.5-1.5B attention shape), head_dim
 128, 16-token blocks, split-K partitions of 512 tokens, 28 independent layer
 caches run back to back (3.76 GB of K/V, far beyond the 256 MB last-level
-cache, so every step reads HBM).  One step = for each of the 28 layers:
-fused RoPE + KV-cache store of the step's 16 new tokens, the split-K
-partition kernel, the log-sum-exp combine (pa_decode with partition_size 512
-is exactly the last two).  All inputs are synthetic, seeded, resident in HBM.
+cache, so every step reads HBM).  One step = for each of the 28 layers: RoPE
+and KV-cache store of the step's 16 new tokens, the split-K partitions and
+the log-sum-exp reduce -- pa_decode_step, two launches per layer (the store
+folded into the partition kernel, then the reduce), bit-identical to
+pa_cache_store + pa_decode (also timed, as `separate_calls`).  All inputs are synthetic, seeded, resident in HBM.
 
 Printed: one JSON line.  value = effective KV GB/s of the whole step (K/V
-bytes the 28 layers read / step time).  roofline = the partition kernel
-(dominant) timed per launch with HIP events on its stream, against 8 TB/s.
-cpu_baseline = the CPU oracle on a bounded sample of the same workload.
-Extra keys: decode-only rates, the batch-1 2048-token decode call, the
-continuous-batching step, and the chunked prefill.
+bytes the 28 layers read / step time).  roofline = the step's partition
+kernel (the store folded in; dominant) timed per launch with HIP events on its
+stream, against 8 TB/s.  cpu_baseline = the CPU oracle on a bounded sample of the same
+workload.  Extra keys: the separate calls, the batch-1 2048-token decode call,
+the continuous-batching step, speculative verification, block copies, the
+layer ops and the chunked prefill.
 
 Other modes (for profiling with rocprofv3, committed so profile commands run
 committed files only):
-    python bench.py --mode decode-kernel   # 3 x 28 launches of the partition kernel only
+    python bench.py --mode decode-kernel   # 3 x 28 launches of the step's partition kernel
+    python bench.py --mode partition-kernel  # 3 x 28 launches of the unfused partition kernel
     python bench.py --mode prefill-kernel  # 20 launches of the prefill kernel only
     python bench.py --mode copy-calibration  # torch copy of 1 GiB (FETCH/WRITE_SIZE scale)
 """
@@ -44,6 +47,7 @@ import workloads as W  # noqa: E402
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 LONG_P = W.LONG_PARTITION
+STEP_KERNEL = "decode_kernel<128, 6, true, true, true>"
 
 
 def _sync():
@@ -81,6 +85,17 @@ def make_long_layers(layers, device):
                                                             P, o_part, lse)
         b.meta["combine"] = pa.prepare_decode_combine(o_part, lse, b.context_lens, b.max_context_len,
                                                       P, dout)
+        # the step with the store folded in reads q unrotated; its own copy, so the separate
+        # store's in-place rotation of b.q cannot change what it is given.  pa_decode_step is
+        # exactly these two calls on the same workspace
+        q_raw = b.q.clone()
+        o2 = torch.empty_like(o_part)
+        l2 = torch.empty_like(lse)
+        b.meta["step_partitions"] = pa.prepare_decode_step_partitions(
+            q_raw, b.k, b.v, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.cos_sin,
+            b.scale, b.max_context_len, P, o2, l2)
+        b.meta["step_combine"] = pa.prepare_decode_combine(o2, l2, b.context_lens, b.max_context_len,
+                                                           P, torch.empty_like(dout))
         out.append(b)
     return out
 
@@ -97,6 +112,27 @@ def combine(b):
     b.meta["combine"]()
 
 
+def fused_step(b):
+    b.meta["step_partitions"]()
+    b.meta["step_combine"]()
+
+
+def fused_partitions(b):
+    b.meta["step_partitions"]()
+
+
+def step_kernel_bytes(b):
+    """Algorithmic bytes of one launch of the step's partition kernel (the store
+    folded in): K and V of every context token (the new token's row read from its
+    input instead), the queries, the cos/sin row of each sequence's position, the
+    block table and the lengths read; the new K/V rows written.  The split-K
+    partials are workspace, not counted."""
+    kv = W.kv_bytes_logical(b.context_lens.cpu().numpy(), b.Hkv, b.D)
+    new_rows = b.B * b.Hkv * b.D * 2 * 2
+    return (kv + b.q.numel() * 2 + b.B * b.D * 4 + b.B * (-(-b.max_context_len // 16)) * 4 + b.B * 4
+            + new_rows)
+
+
 def partition_kernel_bytes(b):
     """Algorithmic bytes one partition-kernel launch must read: K and V of every
     context token, the queries, the block table and the context lengths."""
@@ -109,15 +145,26 @@ def partition_kernel_bytes(b):
 # ---------------------------------------------------------------------------
 
 def run_long(layers, steps, warmup):
-    """Three windows over the same prepared calls, each bracketed by one pair of
-    HIP events on the library's stream (torch's current stream):
-      step    store + partitions + combine for every layer  -> the headline value
-      decode  partitions + combine for every layer
-      kernel  the partition launches alone, back to back     -> average launch time
+    """Windows over the same prepared calls, each bracketed by one pair of HIP
+    events on the library's stream (torch's current stream):
+      step      pa_decode_step for every layer (partitions with the store folded
+                in, then the reduce)                             -> value
+      stepk     the step's partition launches alone             -> roofline
+      separate  store + partitions + combine for every layer
+      decode    partitions + combine for every layer
+      kernel    the unfused partition launches alone
     No event sits inside a window, so none adds its own cost to what is timed."""
     L = layers
 
     def step():
+        for b in L:
+            fused_step(b)
+
+    def step_kernel():
+        for b in L:
+            fused_partitions(b)
+
+    def separate():
         for b in L:
             store(b)
             partitions(b)
@@ -144,10 +191,10 @@ def run_long(layers, steps, warmup):
         _sync()
         return t0.elapsed_time(t1) / steps
 
-    step_ms = window(step)
-    decode_only_ms = window(decode_only)
-    kernel_ms = window(kernel_only)
-    return step_ms, kernel_ms * 1000 / len(L), decode_only_ms
+    return {"step_ms": window(step), "step_kernel_us": window(step_kernel) * 1000 / len(L),
+            "separate_ms": window(separate),
+            "decode_only_ms": window(decode_only),
+            "partition_us": window(kernel_only) * 1000 / len(L)}
 
 
 def run_verify(layers, steps, warmup, nq=5):
@@ -380,7 +427,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--mode", default="bench",
-                    choices=["bench", "decode-kernel", "prefill-kernel", "copy-calibration"])
+                    choices=["bench", "decode-kernel", "partition-kernel", "prefill-kernel",
+                             "copy-calibration"])
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -405,15 +453,16 @@ def main():
         _sync()
         print(json.dumps({"mode": "copy-calibration", "bytes_read": n, "bytes_written": n}))
         return
-    if args.mode == "decode-kernel":
+    if args.mode in ("decode-kernel", "partition-kernel"):
         Ls = make_long_layers(args.layers, dev)
+        fn = fused_partitions if args.mode == "decode-kernel" else partitions
         _sync()
         for _ in range(3):
             for b in Ls:
-                partitions(b)
+                fn(b)
         _sync()
-        print(json.dumps({"mode": "decode-kernel", "launches": 3 * len(Ls),
-                          "bytes_per_launch": partition_kernel_bytes(Ls[0])}))
+        nbytes = step_kernel_bytes(Ls[0]) if args.mode == "decode-kernel" else partition_kernel_bytes(Ls[0])
+        print(json.dumps({"mode": args.mode, "launches": 3 * len(Ls), "bytes_per_launch": nbytes}))
         return
     if args.mode == "prefill-kernel":
         b = W.chunked_prefill(device=dev)
@@ -428,12 +477,16 @@ def main():
 
     layers = make_long_layers(args.layers, dev)
     _sync()
-    step_ms, part_avg_us, decode_only_ms = run_long(layers, args.steps, args.warmup)
+    t = run_long(layers, args.steps, args.warmup)
+    step_ms = t["step_ms"]
+    nl = len(layers)
     kv_step = sum(W.kv_bytes_logical(b.context_lens.cpu().numpy(), b.Hkv, b.D) for b in layers)
     value = kv_step / (step_ms * 1e-3) / 1e9
-    launch_bytes = partition_kernel_bytes(layers[0])
-    achieved = launch_bytes / (part_avg_us * 1e-6) / 1e9
-    traffic = load_traffic("k_decode.hip", "decode_kernel<128, 6, true, true>")
+    launch_us = t["step_kernel_us"]         # the step's partition kernel, back to back
+    launch_bytes = step_kernel_bytes(layers[0])
+    achieved = launch_bytes / (launch_us * 1e-6) / 1e9
+    part_bytes = partition_kernel_bytes(layers[0])
+    traffic = load_traffic("k_decode.hip", STEP_KERNEL)
     line = {
         "metric": "paged-attn decode effective KV GB/s (% of HBM peak); us/call at Qwen2.5-1.5B shape",
         "value": round(value, 1),
@@ -449,18 +502,25 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "long-context flash-decode step: 28 layer caches x (RoPE+store of 16 new "
-                        "tokens, split-K decode, LSE combine)",
+                        "tokens, split-K decode, LSE reduce) = pa_decode_step each (two launches)",
             "batch": layers[0].B, "context_len": layers[0].max_context_len,
             "q_heads": layers[0].Hq, "kv_heads": layers[0].Hkv, "head_dim": layers[0].D,
-            "block_size": 16, "partition_size": LONG_P, "layers": len(layers),
+            "block_size": 16, "partition_size": LONG_P, "layers": nl,
             "kv_bytes_per_step": kv_step,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "us_per_layer_call": round(step_ms * 1000 / len(layers), 2),
-        "decode_only": {"us_per_layer_call": round(decode_only_ms * 1000 / len(layers), 2),
-                        "kv_GBps": round(kv_step / (decode_only_ms * 1e-3) / 1e9, 1)},
+        "us_per_layer_call": round(step_ms * 1000 / nl, 2),
+        "separate_calls": {
+            "note": "pa_cache_store + pa_decode (partitions, reduce): three launches per layer, same results",
+            "us_per_layer": round(t["separate_ms"] * 1000 / nl, 2),
+            "kv_GBps": round(kv_step / (t["separate_ms"] * 1e-3) / 1e9, 1),
+            "decode_only_us_per_layer": round(t["decode_only_ms"] * 1000 / nl, 2),
+            "partition_kernel_avg_us": round(t["partition_us"], 3),
+            "partition_kernel_GBps": round(part_bytes / (t["partition_us"] * 1e-6) / 1e9, 1),
+            "partition_kernel_frac": round(part_bytes / (t["partition_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        },
         "roofline": {
-            "kernel": "decode_kernel<128, 6, true, true> (split-K partitions)",
+            "kernel": STEP_KERNEL + " (split-K partitions with the RoPE + store of the new token)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -468,8 +528,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "bytes_per_launch": launch_bytes,
-            "avg_launch_us": round(part_avg_us, 3),
-            "launches_timed": args.steps * len(layers),
+            "avg_launch_us": round(launch_us, 3),
+            "launches_timed": args.steps * nl,
         },
     }
     if not args.no_context:

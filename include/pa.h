@@ -226,6 +226,55 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
                           pa_stream_t stream);
 
 /*
+ * The decode step with the store folded into the decode kernel ([Pico-vLLM]
+ * §2: fused RoPE + KV-cache store and the paged decode kernel; "H200
+ * comparison": Flash Decode's split and reduce; [mini-llm] §3.1: the new
+ * token's row in its 16-token block).  For every sequence b with
+ * L_b = context_lens[b] > 0 the new token sits at position L_b - 1:
+ *   1. its k (rotated) and v are written to row (L_b-1) % 16 of block
+ *      block_tables[b][(L_b-1) / 16] of every KV head, as pa_cache_store with
+ *      slot = that row and position = L_b - 1 would write them;
+ *   2. out[b] = pa_decode of the rotated q over the L_b tokens, new one
+ *      included, with the same partition size and the same reduce.
+ * The results (out and the pools) are bit-identical to pa_cache_store
+ * followed by pa_decode; the step takes two launches (one with a single
+ * pass) instead of three.  q is only read (the separate store rotates it in
+ * place; this call does not).  L_b = 0: out[b] is zero and nothing is written.
+ *
+ * q, k, v          bf16 [B][Hq][D], [B][Hkv][D], [B][Hkv][D]: the new token,
+ *                  not rotated.
+ * cos_sin          fp32 [max_pos][D] as for pa_cache_store; max_pos must be at
+ *                  least max_context_len, else PA_ERR_SHAPE.
+ * other arguments  as for pa_decode, the workspace included
+ *                  (pa_decode_workspace_bytes).
+ * Device-side preconditions as for pa_decode, plus: the new token's block is
+ * owned by its sequence alone (ref_count 1: copy-on-write first) and L_b - 1
+ * < max_pos.
+ */
+pa_status pa_decode_step(void* out, const void* q, const void* k, const void* v, void* k_cache,
+                         void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                         const float* cos_sin, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t block_size, int32_t max_blocks, int32_t max_context_len,
+                         int32_t max_pos, float scale, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, pa_stream_t stream);
+
+/*
+ * The first stage of pa_decode_step with partition_size > 0: the store of the
+ * new token folded into pa_decode_partitions.  It writes the new K/V rows
+ * exactly as pa_decode_step does and o_part / lse exactly as
+ * pa_decode_partitions would after pa_cache_store; pa_decode_combine then
+ * gives pa_decode_step's out.  Arguments as for pa_decode_step and
+ * pa_decode_partitions.
+ */
+pa_status pa_decode_step_partitions(float* o_part, float* lse, const void* q, const void* k,
+                                    const void* v, void* k_cache, void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    const float* cos_sin, int32_t B, int32_t Hq, int32_t Hkv,
+                                    int32_t D, int32_t block_size, int32_t max_blocks,
+                                    int32_t max_context_len, int32_t max_pos, float scale,
+                                    int32_t partition_size, pa_stream_t stream);
+
+/*
  * Copy-on-write block copies inside one pair of pools ([mini-llm] §3.4: a
  * block shared by several sequences, ref_count > 1, is copied to a freshly
  * allocated block before one of them writes it).  For every i < n, the whole

@@ -48,6 +48,10 @@ _SIGS = {
                                       _i64, _i32, _p]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_partition_size": (_i32, [_i32, _i32, _i32]),
+    "pa_decode_step": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                      _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
+    "pa_decode_step_partitions": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32,
+                                                 _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p]),
     "pa_decode": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _f32, _i32, _p, _sz, _p]),
     "pa_decode_partitions": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
@@ -253,6 +257,87 @@ def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_c
                               _ptr(context_lens), B, hq, hkv, d, bs, mb, int(max_context_len),
                               float(scale), P, _ptr(workspace), wbytes, _stream(dev)),
                 result=out, keep=(q, k_cache, v_cache, block_tables, context_lens, workspace))
+
+
+def decode_step(q, k, v, k_cache, v_cache, block_tables, context_lens, cos_sin, scale,
+                max_context_len, partition_size=-1, out=None, workspace=None):
+    """The decode step with the store folded into the decode kernel (pa_decode_step):
+    the new token (q, k, v not rotated, one per sequence, at position L-1) is rotated,
+    its K/V row stored in the cache, and out = attention over the L tokens; the same
+    results as cache_store + decode.  q is not modified.  Returns out bf16 [B, Hq, D]."""
+    return prepare_decode_step(q, k, v, k_cache, v_cache, block_tables, context_lens, cos_sin,
+                               scale, max_context_len, partition_size, out, workspace)()
+
+
+def prepare_decode_step(q, k, v, k_cache, v_cache, block_tables, context_lens, cos_sin, scale,
+                        max_context_len, partition_size=-1, out=None, workspace=None):
+    """Validated pa_decode_step call (see decode_step); allocates out/workspace once."""
+    dev, B, hq, hkv, d, bs, mb = _decode_common(q, k_cache, v_cache, block_tables, context_lens)
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, torch.bfloat16, 3, dev)
+        if t.shape != (B, hkv, d):
+            raise ValueError(f"{name} must be [B, Hkv, D] matching the cache")
+    _check(cos_sin, "cos_sin", torch.float32, 2, dev)
+    if cos_sin.shape[1] != d:
+        raise ValueError("cos_sin must be [max_pos, D]")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", torch.bfloat16, 3, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    P = decode_partition_size(B, hkv, max_context_len) if partition_size == -1 else partition_size
+    need = decode_workspace_bytes(B, hq, hkv, d, max_context_len, P) if P > 0 else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check(workspace, "workspace", workspace.dtype, None, dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return Call("pa_decode_step", (_ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(block_tables), _ptr(context_lens), _ptr(cos_sin), B, hq, hkv,
+                                   d, bs, mb, int(max_context_len), cos_sin.shape[0], float(scale), P,
+                                   _ptr(workspace), wbytes, _stream(dev)),
+                result=out, keep=(q, k, v, k_cache, v_cache, block_tables, context_lens, cos_sin,
+                                  workspace))
+
+
+def decode_step_partitions(q, k, v, k_cache, v_cache, block_tables, context_lens, cos_sin, scale,
+                           max_context_len, partition_size, o_part=None, lse=None):
+    """First stage of decode_step (pa_decode_step_partitions): the store folded into the
+    split-K partition kernel.  Returns (o_part fp32 [B, Hq, NP, D], lse fp32 [B, Hq, NP])."""
+    return prepare_decode_step_partitions(q, k, v, k_cache, v_cache, block_tables, context_lens,
+                                          cos_sin, scale, max_context_len, partition_size, o_part,
+                                          lse)()
+
+
+def prepare_decode_step_partitions(q, k, v, k_cache, v_cache, block_tables, context_lens, cos_sin,
+                                   scale, max_context_len, partition_size, o_part=None, lse=None):
+    """Validated pa_decode_step_partitions call (see decode_step_partitions)."""
+    dev, B, hq, hkv, d, bs, mb = _decode_common(q, k_cache, v_cache, block_tables, context_lens)
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, torch.bfloat16, 3, dev)
+        if t.shape != (B, hkv, d):
+            raise ValueError(f"{name} must be [B, Hkv, D] matching the cache")
+    _check(cos_sin, "cos_sin", torch.float32, 2, dev)
+    if cos_sin.shape[1] != d:
+        raise ValueError("cos_sin must be [max_pos, D]")
+    P = int(partition_size)
+    if P <= 0:
+        raise ValueError("partition_size must be a positive multiple of 16")
+    np_ = max(1, -(-int(max_context_len) // P))
+    if o_part is None:
+        o_part = torch.empty((B, hq, np_, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, hq, np_), dtype=torch.float32, device=dev)
+    _check(o_part, "o_part", torch.float32, 4, dev)
+    _check(lse, "lse", torch.float32, 3, dev)
+    if tuple(o_part.shape) != (B, hq, np_, d) or tuple(lse.shape) != (B, hq, np_):
+        raise ValueError("o_part / lse have the wrong shape")
+    return Call("pa_decode_step_partitions",
+                (_ptr(o_part), _ptr(lse), _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
+                 _ptr(block_tables), _ptr(context_lens), _ptr(cos_sin), B, hq, hkv, d, bs, mb,
+                 int(max_context_len), cos_sin.shape[0], float(scale), P, _stream(dev)),
+                result=(o_part, lse),
+                keep=(q, k, v, k_cache, v_cache, block_tables, context_lens, cos_sin))
 
 
 def decode_multi_workspace_bytes(B, NQ, Hq, Hkv, D, max_context_len, partition_size=-1):

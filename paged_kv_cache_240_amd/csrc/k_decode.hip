@@ -72,15 +72,173 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Log-sum-exp combine of split-K partials (Flash Decode's reduce) for one
+// query row of a sequence of L tokens, by one wave (lane = 0..63); a row is a
+// query head (or, for multi-query decode, a (query, head) pair).  Every load
+// is issued before L is used: lane j < num_parts reads lse[j] and each lane
+// reads one 16-byte piece of every partial it may need (indices clamped into
+// the workspace); partitions past ceil(L / P) were never written and are
+// removed by selects, not arithmetic, so stale workspace contents (NaN
+// included) cannot leak.  Then: M = max lse,
+// out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M).
+template <int D, int MAXP>
+__device__ __forceinline__ void combine_row(uint16_t* __restrict__ out, const float* __restrict__ o_part,
+                                            const float* __restrict__ lse, int L, int64_t row,
+                                            int num_parts, int part_tokens, int lane) {
+  constexpr int PIECES = D / 4;     // float4 pieces of one partial row
+  constexpr int PPI = 64 / PIECES;  // partials covered by one wave-wide step
+  constexpr int NSTEP = MAXP / PPI;
+  const int piece = lane % PIECES, sub = lane / PIECES;
+  const float* ls = lse + row * num_parts;
+  const float* src = o_part + row * num_parts * D + piece * 4;
+  const float my_lse = ls[min(lane, num_parts - 1)];
+  float4 t[NSTEP];
+  float tl[NSTEP];
+#pragma unroll
+  for (int k = 0; k < NSTEP; ++k) {
+    const int i = min(sub + PPI * k, num_parts - 1);
+    t[k] = *reinterpret_cast<const float4*>(src + (int64_t)i * D);
+    tl[k] = ls[i];
+  }
+  uint16_t* o = out + row * D + piece * 4;
+  if (L <= 0) {
+    if (sub == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
+    return;
+  }
+  const int n = (L + part_tokens - 1) / part_tokens;
+  const float M = wave_max(lane < n ? my_lse : -INFINITY);
+  if (M == -INFINITY) {  // no partition saw a key of this row (multi-query rows before the cache)
+    if (sub == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
+    return;
+  }
+  const float W = wave_sum(lane < n ? exp2f(my_lse - M) : 0.f);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < NSTEP; ++k) {
+    const bool in = sub + PPI * k < n;
+    const float w = in ? exp2f(tl[k] - M) : 0.f;
+    acc.x += in ? w * t[k].x : 0.f; acc.y += in ? w * t[k].y : 0.f;
+    acc.z += in ? w * t[k].z : 0.f; acc.w += in ? w * t[k].w : 0.f;
+  }
+  if constexpr (PPI >= 4) {
+    acc.x += swap16(acc.x); acc.y += swap16(acc.y); acc.z += swap16(acc.z); acc.w += swap16(acc.w);
+  }
+  acc.x += swap32(acc.x); acc.y += swap32(acc.y); acc.z += swap32(acc.z); acc.w += swap32(acc.w);
+  if (sub == 0) {
+    const float inv = 1.f / W;
+    *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv),
+                                              pack_bf16x2(acc.z * inv, acc.w * inv));
+  }
+}
+
+// The same reduce for more than 64 partitions: loops over the partitions.
+template <int D>
+__device__ __forceinline__ void combine_row_many(uint16_t* __restrict__ out, const float* __restrict__ o_part,
+                                                 const float* __restrict__ lse, int L, int64_t row,
+                                                 int num_parts, int part_tokens, int lane) {
+  constexpr int PIECES = D / 4;
+  constexpr int PPI = 64 / PIECES;
+  const int piece = lane % PIECES, sub = lane / PIECES;
+  uint16_t* o = out + row * D + piece * 4;
+  if (L <= 0) {
+    if (sub == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
+    return;
+  }
+  const int n = (L + part_tokens - 1) / part_tokens;
+  const float* ls = lse + row * num_parts;
+  float M = -INFINITY;
+  for (int i = lane; i < n; i += 64) M = fmaxf(M, ls[i]);
+  M = wave_max(M);
+  if (M == -INFINITY) {  // no partition saw a key of this row
+    if (sub == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
+    return;
+  }
+  float W = 0.f;
+  for (int i = lane; i < n; i += 64) W += exp2f(ls[i] - M);
+  W = wave_sum(W);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* src = o_part + row * num_parts * D + piece * 4;
+#pragma unroll 8
+  for (int i = sub; i < n; i += PPI) {
+    const float w = exp2f(ls[i] - M);
+    const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)i * D);
+    acc.x = fmaf(w, t.x, acc.x); acc.y = fmaf(w, t.y, acc.y);
+    acc.z = fmaf(w, t.z, acc.z); acc.w = fmaf(w, t.w, acc.w);
+  }
+  if constexpr (PPI >= 4) {
+    acc.x += swap16(acc.x); acc.y += swap16(acc.y); acc.z += swap16(acc.z); acc.w += swap16(acc.w);
+  }
+  acc.x += swap32(acc.x); acc.y += swap32(acc.y); acc.z += swap32(acc.z); acc.w += swap32(acc.w);
+  if (sub == 0) {
+    const float inv = 1.f / W;
+    *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv),
+                                              pack_bf16x2(acc.z * inv, acc.w * inv));
+  }
+}
+
+// Inputs of the fused decode step (FUSED kernels only): the new token of
+// every sequence, not yet rotated, and the rotation table.
+struct StepArgs {
+  const uint16_t* k_new;  // bf16 [B][Hkv][D]
+  const uint16_t* v_new;  // bf16 [B][Hkv][D]
+  const float* cos_sin;   // fp32 [max_pos][D]: cos | sin of each position
+};
+
+// Rotate-half RoPE of 8 consecutive dims j..j+7 of the first half (a) and
+// their partners j+D/2.. (b): lo = a cos - b sin, hi = b cos + a sin, each
+// product and each sum rounded to fp32 on its own (no fused multiply-add),
+// then rounded to bf16 to nearest even: the operation order of the fused
+// RoPE + store kernel, so both produce the same bits.
+__device__ __forceinline__ void rope_rotate8(const uint4 a, const uint4 b, const float (&c)[8],
+                                             const float (&sn)[8], uint4& lo, uint4& hi) {
+#pragma clang fp contract(off)
+  float fa[8], fb[8], l[8], h[8];
+  unpack_bf16x8(a, fa);
+  unpack_bf16x8(b, fb);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float ac = fa[e] * c[e];
+    const float bs = fb[e] * sn[e];
+    const float bc = fb[e] * c[e];
+    const float as = fa[e] * sn[e];
+    l[e] = ac - bs;
+    h[e] = bc + as;
+  }
+  lo = pack_bf16x8(l);
+  hi = pack_bf16x8(h);
+}
+
+// Fused step, V of the new token's block or of a block past the range (which
+// re-reads it): rows from r_new on take the new row (row r_new itself, and the
+// rows past the range, which only meet p = 0 and would otherwise read row 0 --
+// the new row's stale slot when r_new is 0).  A lane holds rows 4*quad ..
+// 4*quad+3, HALF dwords each.
+template <int SLOT, int HALF>
+__device__ __forceinline__ void substitute_v_rows(uint32_t (&slot)[SLOT], const uint32_t* vrow,
+                                                  int lane, int r_new) {
+  const int quad = lane >> 4;
+  uint32_t v[HALF];
+#pragma unroll
+  for (int w = 0; w < HALF; ++w) v[w] = vrow[w * 64 + lane];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int w = 0; w < HALF; ++w)
+      slot[r * HALF + w] = 4 * quad + r >= r_new ? v[w] : slot[r * HALF + w];
+}
+
 // ONE: the range is a single chunk (split-K with partitions of at most 512
 // tokens), so the ring need not cycle and can be deeper; no refills past it.
-template <int D, int G, bool SPLIT, bool ONE>
+// FUSED: the decode step's store folded in (see launch_decode_step): q and
+// the new k arrive unrotated, and the new token's K/V row is written to the
+// cache and used from registers.
+template <int D, int G, bool SPLIT, bool ONE, bool FUSED>
 __global__ void __launch_bounds__(256, 2)  // 2 waves per SIMD: 8 streaming waves per CU
 decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
               const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
               const int32_t* __restrict__ context_lens, int Hkv, int max_blocks,
               float scale_log2, int part_tokens, int num_parts, uint16_t* __restrict__ out,
-              float* __restrict__ o_part, float* __restrict__ lse) {
+              float* __restrict__ o_part, float* __restrict__ lse, const StepArgs st) {
   static_assert(G >= 1 && G <= 8, "query heads per KV head: 1..8");
   constexpr int KS = D / 32;    // QK k-steps over the head dimension
   constexpr int DPL = D / 16;   // PV: dims per lane = output tiles of 16 columns
@@ -93,6 +251,10 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
 
   __shared__ __align__(16) float red[kWaves][G][D];  // per-wave outputs, dim n*DPL+s at s*16+n
   __shared__ float st_m[kWaves][G], st_l[kWaves][G];
+  // fused step: the new V row's pieces, one copy per wave (lane-major), and
+  // the owner wave's new K row, parked between the prologue and their use
+  __shared__ uint32_t new_v[FUSED ? kWaves * HALF * 64 : 1];
+  __shared__ uint32_t new_k[FUSED ? SLOT * 64 : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar table reads
@@ -131,9 +293,54 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
     return;
   }
 
-  uint4 qb[KS];
+  // Fused step: the new token sits at position L-1, row r_new of logical block
+  // nb_new, the last block of the last range (own_wg).  The one wave whose
+  // blocks include it (owner) rotates its k, writes the K/V row to the cache
+  // and substitutes the K row into that block.  Every wave of own_wg
+  // substitutes the V row into that block and into the blocks past the range,
+  // which re-read it and send their rows to its row 0: the new row's stale
+  // slot when r_new is 0.  The loads and the cos/sin row are requested here,
+  // before the ring fill, and consumed after it.
+  const int nb_new = (L - 1) / kBlockSize, r_new = (L - 1) % kBlockSize;
+  const int lb_new = nb_new - (SPLIT ? p * part_tokens / kBlockSize : 0);  // in this range
+  const bool own_wg = FUSED && (!SPLIT || p == (L - 1) / part_tokens);
+  const bool owner = own_wg && wave == lb_new % kWaves;
+  const int c_new = lb_new / kChunkBlocks, i_new = (lb_new % kChunkBlocks) / kWaves;
+  float cs_c[KS / 2][8], cs_s[KS / 2][8];
+  uint4 kraw[KS];
+  uint32_t vraw[HALF];
+  int ent_new = 0;
+  if constexpr (FUSED) {
+    const float* cs = st.cos_sin + (int64_t)(L - 1) * D;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qb[ks] = col < G ? qraw[ks] : make_uint4(0u, 0u, 0u, 0u);
+    for (int ks = 0; ks < KS / 2; ++ks) {
+      const int j = ks * 32 + quad * 8;
+      const float4 c0 = *reinterpret_cast<const float4*>(cs + j);
+      const float4 c1 = *reinterpret_cast<const float4*>(cs + j + 4);
+      const float4 s0 = *reinterpret_cast<const float4*>(cs + D / 2 + j);
+      const float4 s1 = *reinterpret_cast<const float4*>(cs + D / 2 + j + 4);
+      cs_c[ks][0] = c0.x; cs_c[ks][1] = c0.y; cs_c[ks][2] = c0.z; cs_c[ks][3] = c0.w;
+      cs_c[ks][4] = c1.x; cs_c[ks][5] = c1.y; cs_c[ks][6] = c1.z; cs_c[ks][7] = c1.w;
+      cs_s[ks][0] = s0.x; cs_s[ks][1] = s0.y; cs_s[ks][2] = s0.z; cs_s[ks][3] = s0.w;
+      cs_s[ks][4] = s1.x; cs_s[ks][5] = s1.y; cs_s[ks][6] = s1.z; cs_s[ks][7] = s1.w;
+    }
+    if (owner) {
+      const uint16_t* kn = st.k_new + ((int64_t)b * Hkv + g) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kraw[ks] = *reinterpret_cast<const uint4*>(kn + ks * 32 + quad * 8);
+      ent_new = bt_row[nb_new];
+    }
+    if (own_wg) {
+      const uint16_t* vn = st.v_new + ((int64_t)b * Hkv + g) * D + col * DPL;
+      if constexpr (HALF == 4) {
+        const uint4 t = *reinterpret_cast<const uint4*>(vn);
+        vraw[0] = t.x; vraw[1] = t.y; vraw[2] = t.z; vraw[3] = t.w;
+      } else {
+        const uint2 t = *reinterpret_cast<const uint2*>(vn);
+        vraw[0] = t.x; vraw[1] = t.y;
+      }
+    }
+  }
 
   floatx4_t o[DPL];  // O[head 4*quad+e][dim col*DPL+s] in o[s][e]
   floatx4_t lacc = {0.f, 0.f, 0.f, 0.f};  // l of head 4*quad+e (every column the same)
@@ -193,6 +400,48 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
 #pragma unroll
   for (int s = 0; s < DEPTH; ++s) load_step(ring[s], ent_cur, s, rows_left(nt0, s));
 
+  uint4 qb[KS];
+  if constexpr (FUSED) {
+    uint4 qr[KS], kr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks) {
+      rope_rotate8(qraw[ks], qraw[ks + KS / 2], cs_c[ks], cs_s[ks], qr[ks], qr[ks + KS / 2]);
+      if (owner) rope_rotate8(kraw[ks], kraw[ks + KS / 2], cs_c[ks], cs_s[ks], kr[ks], kr[ks + KS / 2]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = col < G ? qr[ks] : make_uint4(0u, 0u, 0u, 0u);
+    if (own_wg) {
+#pragma unroll
+      for (int w = 0; w < HALF; ++w) new_v[(wave * HALF + w) * 64 + lane] = vraw[w];
+    }
+    if (owner) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        new_k[(4 * ks) * 64 + lane] = kr[ks].x;
+        new_k[(4 * ks + 1) * 64 + lane] = kr[ks].y;
+        new_k[(4 * ks + 2) * 64 + lane] = kr[ks].z;
+        new_k[(4 * ks + 3) * 64 + lane] = kr[ks].w;
+      }
+      // the row for later steps (no load of this launch reads it back); the
+      // pools are written only here, through the one row of the new token
+      const int64_t row_off = (int64_t)ent_new * blk_stride + head_off + r_new * D;
+      uint16_t* kw = const_cast<uint16_t*>(k_cache) + row_off;
+      uint16_t* vw = const_cast<uint16_t*>(v_cache) + row_off;
+      if (col == 0)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<uint4*>(kw + ks * 32 + quad * 8) = kr[ks];
+      if (quad == 0) {
+        if constexpr (HALF == 4)
+          *reinterpret_cast<uint4*>(vw + col * DPL) = make_uint4(vraw[0], vraw[1], vraw[2], vraw[3]);
+        else
+          *reinterpret_cast<uint2*>(vw + col * DPL) = make_uint2(vraw[0], vraw[1]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = col < G ? qraw[ks] : make_uint4(0u, 0u, 0u, 0u);
+  }
+
   for (int c = 0; c < nchunks; ++c) {
     const int c0 = t_begin + c * kChunkTokens;
     const int nt = min(kChunkTokens, t_end - c0);  // valid tokens of the chunk
@@ -208,6 +457,12 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
       if constexpr (step < kWaveBlocks) {
         // ---- QK on block i: S^T (16 keys x 16 heads) ---------------------------
         const int left = rows_left(nt, step);
+        if constexpr (FUSED) {
+          if (owner && c == c_new && i == i_new) {
+#pragma unroll
+            for (int d = 0; d < SLOT; ++d) cur[d] = col == r_new ? new_k[d * 64 + lane] : cur[d];
+          }
+        }
         floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -262,6 +517,17 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
           // ---- PV on blocks i-1, i: 32 keys ---------------------------------------
           uint32_t(&va)[SLOT] = ring[(step - 1) % DEPTH];
           uint32_t(&vb)[SLOT] = cur;
+          if constexpr (FUSED) {
+            // blocks i-1, i of this chunk, at or past the new block; two
+            // separate tests on fixed slots: a merged call on a selected slot
+            // address would force the whole ring into memory
+            const int lb_i = c * kChunkBlocks + wave + kWaves * i;  // block i in the range
+            if (own_wg && lb_i - kWaves >= lb_new)
+              substitute_v_rows<SLOT, HALF>(va, new_v + wave * HALF * 64, lane, r_new);
+            __builtin_amdgcn_sched_barrier(0);
+            if (own_wg && lb_i >= lb_new)
+              substitute_v_rows<SLOT, HALF>(vb, new_v + wave * HALF * 64, lane, r_new);
+          }
           const uint4 pj = pa[i / 2];
 #pragma unroll
           for (int s = 0; s < DPL; ++s) {
@@ -343,124 +609,32 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
   }
 }
 
-// Log-sum-exp combine of split-K partials (Flash Decode's reduce): one wave
-// per (query row, sequence), a row being a query head (or, for multi-query
-// decode, a (query, head) pair).  Every load is issued before L is known: lane
-// j < num_parts reads lse[j] and each lane reads one 16-byte piece of every
-// partial it may need (indices clamped into the workspace); partitions past
-// ceil(L / P) were never written and are removed by selects, not arithmetic,
-// so stale workspace contents (NaN included) cannot leak.  Then: M = max lse,
-// out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M).
+// One wave per (query row, sequence).
 template <int D, int MAXP>
 __global__ void __launch_bounds__(64)
 combine_kernel(uint16_t* __restrict__ out, const float* __restrict__ o_part,
                const float* __restrict__ lse, const int32_t* __restrict__ context_lens, int Hq,
                int num_parts, int part_tokens) {
-  constexpr int PIECES = D / 4;     // float4 pieces of one partial row
-  constexpr int PPI = 64 / PIECES;  // partials covered by one wave-wide step
-  constexpr int NSTEP = MAXP / PPI;
   const int h = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int piece = lane % PIECES, sub = lane / PIECES;
-  const int64_t row = (int64_t)b * Hq + h;
-  const float* ls = lse + row * num_parts;
-  const float* src = o_part + row * num_parts * D + piece * 4;
-  const int L = context_lens[b];
-  const float my_lse = ls[min(lane, num_parts - 1)];
-  float4 t[NSTEP];
-  float tl[NSTEP];
-#pragma unroll
-  for (int k = 0; k < NSTEP; ++k) {
-    const int i = min(sub + PPI * k, num_parts - 1);
-    t[k] = *reinterpret_cast<const float4*>(src + (int64_t)i * D);
-    tl[k] = ls[i];
-  }
-  uint16_t* o = out + row * D + piece * 4;
-  if (L <= 0) {
-    if (sub == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
-    return;
-  }
-  const int n = (L + part_tokens - 1) / part_tokens;
-  const float M = wave_max(lane < n ? my_lse : -INFINITY);
-  if (M == -INFINITY) {  // no partition saw a key of this row (multi-query rows before the cache)
-    if (sub == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
-    return;
-  }
-  const float W = wave_sum(lane < n ? exp2f(my_lse - M) : 0.f);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int k = 0; k < NSTEP; ++k) {
-    const bool in = sub + PPI * k < n;
-    const float w = in ? exp2f(tl[k] - M) : 0.f;
-    acc.x += in ? w * t[k].x : 0.f; acc.y += in ? w * t[k].y : 0.f;
-    acc.z += in ? w * t[k].z : 0.f; acc.w += in ? w * t[k].w : 0.f;
-  }
-  if constexpr (PPI >= 4) {
-    acc.x += swap16(acc.x); acc.y += swap16(acc.y); acc.z += swap16(acc.z); acc.w += swap16(acc.w);
-  }
-  acc.x += swap32(acc.x); acc.y += swap32(acc.y); acc.z += swap32(acc.z); acc.w += swap32(acc.w);
-  if (sub == 0) {
-    const float inv = 1.f / W;
-    *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv),
-                                              pack_bf16x2(acc.z * inv, acc.w * inv));
-  }
+  combine_row<D, MAXP>(out, o_part, lse, context_lens[b], (int64_t)b * Hq + h, num_parts,
+                       part_tokens, threadIdx.x);
 }
 
-// Fallback for more than 64 partitions: loops over the partitions.
 template <int D>
 __global__ void __launch_bounds__(64)
 combine_many_kernel(uint16_t* __restrict__ out, const float* __restrict__ o_part,
                     const float* __restrict__ lse, const int32_t* __restrict__ context_lens, int Hq,
                     int num_parts, int part_tokens) {
-  constexpr int PIECES = D / 4;
-  constexpr int PPI = 64 / PIECES;
   const int h = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int piece = lane % PIECES, sub = lane / PIECES;
-  const int64_t row = (int64_t)b * Hq + h;
-  const int L = context_lens[b];
-  uint16_t* o = out + row * D + piece * 4;
-  if (L <= 0) {
-    if (sub == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
-    return;
-  }
-  const int n = (L + part_tokens - 1) / part_tokens;
-  const float* ls = lse + row * num_parts;
-  float M = -INFINITY;
-  for (int i = lane; i < n; i += 64) M = fmaxf(M, ls[i]);
-  M = wave_max(M);
-  if (M == -INFINITY) {  // no partition saw a key of this row
-    if (sub == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
-    return;
-  }
-  float W = 0.f;
-  for (int i = lane; i < n; i += 64) W += exp2f(ls[i] - M);
-  W = wave_sum(W);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* src = o_part + row * num_parts * D + piece * 4;
-#pragma unroll 8
-  for (int i = sub; i < n; i += PPI) {
-    const float w = exp2f(ls[i] - M);
-    const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)i * D);
-    acc.x = fmaf(w, t.x, acc.x); acc.y = fmaf(w, t.y, acc.y);
-    acc.z = fmaf(w, t.z, acc.z); acc.w = fmaf(w, t.w, acc.w);
-  }
-  if constexpr (PPI >= 4) {
-    acc.x += swap16(acc.x); acc.y += swap16(acc.y); acc.z += swap16(acc.z); acc.w += swap16(acc.w);
-  }
-  acc.x += swap32(acc.x); acc.y += swap32(acc.y); acc.z += swap32(acc.z); acc.w += swap32(acc.w);
-  if (sub == 0) {
-    const float inv = 1.f / W;
-    *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv),
-                                              pack_bf16x2(acc.z * inv, acc.w * inv));
-  }
+  combine_row_many<D>(out, o_part, lse, context_lens[b], (int64_t)b * Hq + h, num_parts,
+                      part_tokens, threadIdx.x);
 }
 
-template <int D, int G>
+template <int D, int G, bool FUSED>
 hipError_t launch_dg(void* out, float* o_part, float* lse, const void* q, const void* k_cache,
                      const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
                      int B, int Hkv, int max_blocks, int max_context_len, float scale,
-                     int partition_size, hipStream_t stream) {
+                     int partition_size, const StepArgs& st, hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kc = static_cast<const uint16_t*>(k_cache);
@@ -469,35 +643,37 @@ hipError_t launch_dg(void* out, float* o_part, float* lse, const void* q, const 
   if (partition_size > 0) {
     const int np = (max_context_len + partition_size - 1) / partition_size;
     if (partition_size <= kChunkTokens)
-      hipLaunchKernelGGL((decode_kernel<D, G, true, true>), dim3(np, Hkv, B), dim3(256), 0, stream,
-                         qq, kc, vc, block_tables, context_lens, Hkv, max_blocks, scale_log2,
-                         partition_size, np, oo, o_part, lse);
+      hipLaunchKernelGGL((decode_kernel<D, G, true, true, FUSED>), dim3(np, Hkv, B), dim3(256), 0,
+                         stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks,
+                         scale_log2, partition_size, np, oo, o_part, lse, st);
     else
-      hipLaunchKernelGGL((decode_kernel<D, G, true, false>), dim3(np, Hkv, B), dim3(256), 0, stream,
-                         qq, kc, vc, block_tables, context_lens, Hkv, max_blocks, scale_log2,
-                         partition_size, np, oo, o_part, lse);
+      hipLaunchKernelGGL((decode_kernel<D, G, true, false, FUSED>), dim3(np, Hkv, B), dim3(256), 0,
+                         stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks,
+                         scale_log2, partition_size, np, oo, o_part, lse, st);
   } else {
-    hipLaunchKernelGGL((decode_kernel<D, G, false, false>), dim3(1, Hkv, B), dim3(256), 0, stream, qq, kc,
-                       vc, block_tables, context_lens, Hkv, max_blocks, scale_log2, 0, 1, oo,
-                       o_part, lse);
+    hipLaunchKernelGGL((decode_kernel<D, G, false, false, FUSED>), dim3(1, Hkv, B), dim3(256), 0,
+                       stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks, scale_log2,
+                       0, 1, oo, o_part, lse, st);
   }
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool FUSED>
 hipError_t launch_d(int G, void* out, float* o_part, float* lse, const void* q, const void* k_cache,
                     const void* v_cache, const int32_t* bt, const int32_t* cl, int B, int Hkv,
-                    int mb, int mcl, float scale, int ps, hipStream_t st) {
+                    int mb, int mcl, float scale, int ps, const StepArgs& sa, hipStream_t st) {
+#define PA_DG(GG) return launch_dg<D, GG, FUSED>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, Hkv, mb, mcl, scale, ps, sa, st)
   switch (G) {
-    case 1: return launch_dg<D, 1>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, Hkv, mb, mcl, scale, ps, st);
-    case 2: return launch_dg<D, 2>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, Hkv, mb, mcl, scale, ps, st);
-    case 3: return launch_dg<D, 3>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, Hkv, mb, mcl, scale, ps, st);
-    case 4: return launch_dg<D, 4>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, Hkv, mb, mcl, scale, ps, st);
-    case 5: return launch_dg<D, 5>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, Hkv, mb, mcl, scale, ps, st);
-    case 6: return launch_dg<D, 6>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, Hkv, mb, mcl, scale, ps, st);
-    case 7: return launch_dg<D, 7>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, Hkv, mb, mcl, scale, ps, st);
-    case 8: return launch_dg<D, 8>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, Hkv, mb, mcl, scale, ps, st);
+    case 1: PA_DG(1);
+    case 2: PA_DG(2);
+    case 3: PA_DG(3);
+    case 4: PA_DG(4);
+    case 5: PA_DG(5);
+    case 6: PA_DG(6);
+    case 7: PA_DG(7);
+    case 8: PA_DG(8);
   }
+#undef PA_DG
   return hipErrorInvalidValue;
 }
 
@@ -509,11 +685,35 @@ hipError_t launch_decode(void* out, float* o_part, float* lse, const void* q, co
                          int max_blocks, int max_context_len, float scale, int partition_size,
                          hipStream_t stream) {
   const int G = Hq / Hkv;
+  const StepArgs none{};
   if (D == 128)
-    return launch_d<128>(G, out, o_part, lse, q, k_cache, v_cache, block_tables, context_lens, B,
-                         Hkv, max_blocks, max_context_len, scale, partition_size, stream);
-  return launch_d<64>(G, out, o_part, lse, q, k_cache, v_cache, block_tables, context_lens, B, Hkv,
-                      max_blocks, max_context_len, scale, partition_size, stream);
+    return launch_d<128, false>(G, out, o_part, lse, q, k_cache, v_cache, block_tables, context_lens,
+                                B, Hkv, max_blocks, max_context_len, scale, partition_size, none,
+                                stream);
+  return launch_d<64, false>(G, out, o_part, lse, q, k_cache, v_cache, block_tables, context_lens, B,
+                             Hkv, max_blocks, max_context_len, scale, partition_size, none, stream);
+}
+
+// The decode step with the store folded into the decode kernel: RoPE of q and
+// of the new k, the new token's K/V row written at position L-1 of each
+// sequence's table, attention over the L tokens; split-K partials are then
+// reduced by the combine launch, as for pa_decode.
+hipError_t launch_decode_step(void* out, float* o_part, float* lse, const void* q,
+                              const void* k, const void* v, void* k_cache, void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              const float* cos_sin, int B, int Hq, int Hkv, int D, int max_blocks,
+                              int max_context_len, float scale, int partition_size,
+                              bool with_combine, hipStream_t stream) {
+  const int G = Hq / Hkv;
+  const StepArgs sa{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), cos_sin};
+  const hipError_t e =
+      D == 128 ? launch_d<128, true>(G, out, o_part, lse, q, k_cache, v_cache, block_tables, context_lens,
+                                     B, Hkv, max_blocks, max_context_len, scale, partition_size, sa, stream)
+               : launch_d<64, true>(G, out, o_part, lse, q, k_cache, v_cache, block_tables, context_lens,
+                                    B, Hkv, max_blocks, max_context_len, scale, partition_size, sa, stream);
+  if (e != hipSuccess || partition_size <= 0 || !with_combine) return e;
+  const int np = (max_context_len + partition_size - 1) / partition_size;
+  return launch_decode_combine(out, o_part, lse, context_lens, B, Hkv * G, D, np, partition_size, stream);
 }
 
 hipError_t launch_decode_combine(void* out, const float* o_part, const float* lse,
@@ -526,11 +726,13 @@ hipError_t launch_decode_combine(void* out, const float* o_part, const float* ls
                      context_lens, Hq, num_partitions, partition_size)
   if (D == 128) {
     if (num_partitions <= 16) PA_COMBINE(128, 16);
+    else if (num_partitions <= 32) PA_COMBINE(128, 32);
     else if (num_partitions <= 64) PA_COMBINE(128, 64);
     else hipLaunchKernelGGL(combine_many_kernel<128>, grid, block, 0, stream, oo, o_part, lse,
                             context_lens, Hq, num_partitions, partition_size);
   } else {
     if (num_partitions <= 16) PA_COMBINE(64, 16);
+    else if (num_partitions <= 32) PA_COMBINE(64, 32);
     else if (num_partitions <= 64) PA_COMBINE(64, 64);
     else hipLaunchKernelGGL(combine_many_kernel<64>, grid, block, 0, stream, oo, o_part, lse,
                             context_lens, Hq, num_partitions, partition_size);

@@ -20,16 +20,6 @@ namespace {
 
 constexpr int kNormThreads = 256;
 
-__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
-  f[0] = bf16lo(v.x); f[1] = bf16hi(v.x); f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
-  f[4] = bf16lo(v.z); f[5] = bf16hi(v.z); f[6] = bf16lo(v.w); f[7] = bf16hi(v.w);
-}
-
-__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
-  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                    pack_bf16x2(f[6], f[7]));
-}
-
 // A row's pieces stay in registers between the sum of squares and the scaling:
 // PER = pieces of 8 values per thread (H <= 8 * PER * kNormThreads).
 template <int PER, bool RESID>
@@ -48,13 +38,13 @@ rmsnorm_kernel(uint16_t* __restrict__ out, uint16_t* __restrict__ residual,
   for (int k = 0; k < PER; ++k) {
     const int i = threadIdx.x + k * kNormThreads;
     if (i < n8) {
-      unpack8(xr[i], v[k]);
+      unpack_bf16x8(xr[i], v[k]);
       if (RESID) {
         float r[8];
-        unpack8(rr[i], r);
+        unpack_bf16x8(rr[i], r);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[k][e] = bf16lo(f32_to_bf16_rne(v[k][e] + r[e]));
-        rr[i] = pack8(v[k]);
+        rr[i] = pack_bf16x8(v[k]);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = fmaf(v[k][e], v[k][e], ss);
@@ -74,10 +64,10 @@ rmsnorm_kernel(uint16_t* __restrict__ out, uint16_t* __restrict__ residual,
     const int i = threadIdx.x + k * kNormThreads;
     if (i < n8) {
       float w[8];
-      unpack8(wr[i], w);
+      unpack_bf16x8(wr[i], w);
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[e] = w[e] * (v[k][e] * inv);
-      orow[i] = pack8(w);
+      orow[i] = pack_bf16x8(w);
     }
   }
 }
@@ -96,8 +86,8 @@ constexpr float kNegLog2e = -1.44269504088896341f;
 
 __device__ __forceinline__ uint4 swiglu_piece(const uint4 gw, const uint4 uw) {
   float g[8], u[8], y[8], a[8];
-  unpack8(gw, g);
-  unpack8(uw, u);
+  unpack_bf16x8(gw, g);
+  unpack_bf16x8(uw, u);
   float amax = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {

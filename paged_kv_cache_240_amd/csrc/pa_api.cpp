@@ -197,6 +197,55 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   return from_hip(pa::launch_decode_combine(out, o_part, lse, context_lens, B, Hq, D, (int)np, P, s));
 }
 
+pa_status pa_decode_step(void* out, const void* q, const void* k, const void* v, void* k_cache,
+                         void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                         const float* cos_sin, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t block_size, int32_t max_blocks, int32_t max_context_len,
+                         int32_t max_pos, float scale, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, pa_stream_t stream) {
+  if (!out || !k || !v || !cos_sin) return PA_ERR_NULL;
+  pa_status st = check_decode(q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, D,
+                              block_size, max_blocks, max_context_len);
+  if (st != PA_OK) return st;
+  if (partition_size < -1 || (partition_size > 0 && partition_size % 16 != 0)) return PA_ERR_SHAPE;
+  if (max_pos < max_context_len) return PA_ERR_SHAPE;
+  const int32_t P = resolve_partition(partition_size, B, Hkv, max_context_len);
+  if (B == 0) return PA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (P == 0 || max_context_len == 0)
+    return from_hip(pa::launch_decode_step(out, nullptr, nullptr, q, k, v, k_cache, v_cache,
+                                           block_tables, context_lens, cos_sin, B, Hq, Hkv, D,
+                                           max_blocks, max_context_len, scale, 0, true, s));
+  const size_t need = pa_decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, P);
+  if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  const int64_t np = ceil_div(max_context_len, P);
+  float* o_part = static_cast<float*>(workspace);
+  float* lse = o_part + (int64_t)B * Hq * np * D;
+  return from_hip(pa::launch_decode_step(out, o_part, lse, q, k, v, k_cache, v_cache,
+                                         block_tables, context_lens, cos_sin, B, Hq, Hkv, D,
+                                         max_blocks, max_context_len, scale, P, true, s));
+}
+
+pa_status pa_decode_step_partitions(float* o_part, float* lse, const void* q, const void* k,
+                                    const void* v, void* k_cache, void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    const float* cos_sin, int32_t B, int32_t Hq, int32_t Hkv,
+                                    int32_t D, int32_t block_size, int32_t max_blocks,
+                                    int32_t max_context_len, int32_t max_pos, float scale,
+                                    int32_t partition_size, pa_stream_t stream) {
+  if (!o_part || !lse || !k || !v || !cos_sin) return PA_ERR_NULL;
+  pa_status st = check_decode(q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, D,
+                              block_size, max_blocks, max_context_len);
+  if (st != PA_OK) return st;
+  if (partition_size <= 0 || partition_size % 16 != 0) return PA_ERR_SHAPE;
+  if (max_pos < max_context_len) return PA_ERR_SHAPE;
+  if (B == 0 || max_context_len == 0) return PA_OK;
+  return from_hip(pa::launch_decode_step(nullptr, o_part, lse, q, k, v, k_cache, v_cache,
+                                         block_tables, context_lens, cos_sin, B, Hq, Hkv, D,
+                                         max_blocks, max_context_len, scale, partition_size, false,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 size_t pa_decode_multi_workspace_bytes(int32_t B, int32_t NQ, int32_t Hq, int32_t Hkv, int32_t D,
                                        int32_t max_context_len, int32_t partition_size) {
   if (NQ <= 0) return 0;

@@ -29,6 +29,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Eight bf16 in a 16-byte piece <-> fp32 (exact widening; narrowing rounds
+// to nearest even with the integer rounding above).
+__device__ __forceinline__ void unpack_bf16x8(const uint4 v, float (&f)[8]) {
+  f[0] = bf16lo(v.x); f[1] = bf16hi(v.x); f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
+  f[4] = bf16lo(v.z); f[5] = bf16hi(v.z); f[6] = bf16lo(v.w); f[7] = bf16hi(v.w);
+}
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&f)[8]) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
 // Interleave two packed bf16 pairs: (a.lo, b.lo) and (a.hi, b.hi).
 __device__ __forceinline__ uint32_t interleave_lo(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);

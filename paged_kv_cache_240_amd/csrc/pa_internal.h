@@ -21,6 +21,17 @@ hipError_t launch_decode(void* out, float* o_part, float* lse, const void* q, co
                          int max_blocks, int max_context_len, float scale, int partition_size,
                          hipStream_t stream);
 
+// The decode step with the store folded into the decode kernel: RoPE of q
+// and of the new k, the new token's K/V row stored at position L-1, attention;
+// with partition_size > 0 the partials are then reduced by the combine launch
+// (with_combine) or left in o_part / lse.
+hipError_t launch_decode_step(void* out, float* o_part, float* lse, const void* q,
+                              const void* k, const void* v, void* k_cache, void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              const float* cos_sin, int B, int Hq, int Hkv, int D, int max_blocks,
+                              int max_context_len, float scale, int partition_size,
+                              bool with_combine, hipStream_t stream);
+
 // Multi-query (speculative verification) partial kernel or single pass: q/out
 // are [B][NQ][Hq][D]; the partials are reduced by launch_decode_combine over
 // NQ * Hq rows per sequence.

@@ -26,6 +26,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("pa_cache_store", "pa_decode", "pa_decode_partitions", "pa_decode_combine",
+              "pa_decode_step", "pa_decode_step_partitions",
               "pa_decode_workspace_bytes", "pa_decode_partition_size", "pa_prefill",
               "pa_decode_multi", "pa_decode_multi_workspace_bytes",
               "pa_status_str"):
@@ -210,3 +211,30 @@ def test_rmsnorm_validation(args, code):
 ])
 def test_swiglu_validation(args, code):
     assert pa.load().pa_swiglu(*args, None) == code
+
+
+def _step(**kw):
+    a = dict(out=P, q=P, k=P, v=P, kc=P, vc=P, bt=P, cl=P, cs=P, B=2, Hq=12, Hkv=2, D=128, bs=16,
+             mb=8, mcl=128, max_pos=128, scale=0.088, ps=-1, ws=None, wsb=0)
+    a.update(kw)
+    return pa.load().pa_decode_step(a["out"], a["q"], a["k"], a["v"], a["kc"], a["vc"], a["bt"],
+                                    a["cl"], a["cs"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                    a["mb"], a["mcl"], a["max_pos"], a["scale"], a["ps"], a["ws"],
+                                    a["wsb"], None)
+
+
+WS16 = 2 * 12 * 8 * 129 * 4   # the pa_decode workspace at B=2, Hq=12, D=128, 128 tokens, P=16
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), NULL), (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL),
+    (dict(kc=None), NULL), (dict(vc=None), NULL), (dict(bt=None), NULL), (dict(cl=None), NULL),
+    (dict(cs=None), NULL),
+    (dict(B=-1), SHAPE), (dict(Hq=7), SHAPE), (dict(D=80), UNSUP), (dict(bs=8), UNSUP),
+    (dict(mb=0), SHAPE), (dict(mcl=129), SHAPE), (dict(max_pos=127), SHAPE),
+    (dict(ps=24), SHAPE), (dict(ps=-2), SHAPE),
+    (dict(ps=16, ws=None, wsb=0), WS), (dict(ps=16, ws=P, wsb=WS16 - 1), WS),
+    (dict(Hq=20, Hkv=2), UNSUP), (dict(B=0), OK),
+])
+def test_decode_step_validation(kw, code):
+    assert _step(**kw) == code
