@@ -6,13 +6,18 @@ prefix reuse, copy-on-write and swap come from the block manager).
 No model and no weights: a token's K and V rows are a fixed pseudo-random
 function of (token id, position), so equal prefixes have equal K/V and cached
 blocks are valid to reuse; queries are fresh random rows each step.  Each step
-runs, in order: the copy-on-write block copies the manager asked for, one
-fused RoPE + store of every new token, pa_prefill for the sequences being
-prefilled (only their uncached prompt tokens) and pa_decode for the others.
+runs, in order: the copy-on-write block copies the manager asked for, the
+fused RoPE + store of the prefill rows, pa_prefill for the sequences being
+prefilled (only their uncached prompt tokens) and pa_decode_step (store
+folded into the decode kernel) for the others.
 Sampling is a seeded draw of the next token id.
 
 `run` yields one record per step (the rows stored and the outputs), so a test
 can check every output against plain unpaged attention.
+
+Decode rows go through pa_decode_step, which stores the new token at the
+position its block table gives (no slot mapping), so the loop also checks
+that the slot the manager hands out and its table agree.
 """
 
 from dataclasses import dataclass, field
@@ -158,22 +163,28 @@ class Loop:
             pos_idx = torch.tensor([r[1] for r in rows])
             k = self.k_tab[tok_idx, pos_idx].to(self.dev)
             v = self.v_tab[tok_idx, pos_idx].to(self.dev)
-            slots = self._ids([r[3] for r in rows])
-            positions = self._ids([r[1] for r in rows])
-            pa.cache_store(q, k, v, self.kc, self.vc, slots, positions, self.cos_sin)
             out_p = out_d = None
             if prefill:
-                qp = torch.cat([q[s:s + n] for _, s, n, _ in prefill]).contiguous()
+                pre_rows = [i for _, s0, n, _ in prefill for i in range(s0, s0 + n)]
+                idx = torch.tensor(pre_rows, device=self.dev)
+                qp = q[idx].contiguous()
+                pa.cache_store(qp, k[idx].contiguous(), v[idx].contiguous(), self.kc, self.vc,
+                               self._ids([rows[i][3] for i in pre_rows]),
+                               self._ids([rows[i][1] for i in pre_rows]), self.cos_sin)
                 bt = self._tables([p[0] for p in prefill])
                 lens = self._ids([p[3] for p in prefill])
                 qsl = self._ids(np.concatenate([[0], np.cumsum([p[2] for p in prefill])]).tolist())
                 out_p = pa.prefill(qp, self.kc, self.vc, bt, lens, qsl, self.scale,
                                    max(p[2] for p in prefill))
             if decode:
-                qd = torch.stack([q[s] for _, s, _ in decode]).contiguous()
+                idx = torch.tensor([s0 for _, s0, _ in decode], device=self.dev)
                 bt = self._tables([d[0] for d in decode])
                 lens = self._ids([d[2] for d in decode])
-                out_d = pa.decode(qd, self.kc, self.vc, bt, lens, self.scale, max(d[2] for d in decode))
+                for (rid, row, L), t in zip(decode, bt.cpu().numpy()):
+                    assert rows[row][3] == t[(L - 1) // 16] * 16 + (L - 1) % 16, "slot and table disagree"
+                out_d = pa.decode_step(q[idx].contiguous(), k[idx].contiguous(), v[idx].contiguous(),
+                                       self.kc, self.vc, bt, lens, self.cos_sin, self.scale,
+                                       max(d[2] for d in decode))
             # the stored tokens are computed: register their full blocks
             for rid in {r[0] for r in rows}:
                 self.bm.commit(rid, self.bm.seq_len(rid))
