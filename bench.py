@@ -245,8 +245,54 @@ def time_calls(fn, reps, warm=10):
     return e0.elapsed_time(e1) * 1000 / reps
 
 
+def time_each(fn, reps, scrub=None, warm=10):
+    """Per-call times in us (one pair of HIP events around each call), as
+    median / p10 / p90.  With scrub (a device tensor of 1 GiB), the tensor is
+    rewritten before every call, outside the timed window, so the call starts
+    with cold caches (the 256 MB last-level cache included)."""
+    for _ in range(warm):
+        fn()
+    _sync()
+    t = []
+    e0, e1 = _event(), _event()
+    for _ in range(reps):
+        if scrub is not None:
+            scrub.add_(1)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        t.append(e0.elapsed_time(e1) * 1000)
+    t = np.sort(np.array(t))
+    return {"median_us": round(float(np.median(t)), 2), "p10_us": round(float(np.percentile(t, 10)), 2),
+            "p90_us": round(float(np.percentile(t, 90)), 2), "reps": reps}
+
+
+def run_ceilings(device):
+    """Measured device limits beside the published ones: a streaming read of a
+    2 GiB buffer (eight times the last-level cache; best of three grid sizes)
+    and bf16 matrix-core throughput (4 independent chains per wave)."""
+    res = {"nominal_hbm_GBps": HBM_PEAK_GBPS, "nominal_mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFLOPS}
+    nbytes = 1 << 31
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=device)
+    best = 0.0
+    for grid in (1024, 2048, 4096):
+        us = time_calls(pa.prepare_probe_stream_read(buf, grid), 10, warm=2)
+        best = max(best, nbytes / us / 1e3)
+    del buf
+    res["stream_read_GBps"] = round(best, 1)
+    iters, best = 20000, 0.0
+    for grid in (512, 1024):
+        us = time_calls(pa.prepare_probe_mfma_bf16(iters, grid, device), 3, warm=1)
+        best = max(best, grid * 4 * iters * 4 * 16384 / us / 1e6)
+    res["mfma_bf16_TFLOPs"] = round(best, 1)
+    res["note"] = "pa_probe_stream_read / pa_probe_mfma_bf16 on this device"
+    return res
+
+
 def run_context(device):
     res = {}
+    scrub = torch.zeros(1 << 28, dtype=torch.int32, device=device)  # 1 GiB
     # batch 1, 2048 tokens: store + decode, library-chosen partitions, warm
     b = W.qwen_decode(device=device)
     P = pa.decode_partition_size(b.B, b.Hkv, b.max_context_len)
@@ -262,7 +308,11 @@ def run_context(device):
     us = time_calls(dec, 1000)
     res["qwen_b1_l2048"] = {"decode_us_per_call": round(us, 2), "partition_size": P,
                             "store_plus_decode_us": round(time_calls(step2, 1000), 2),
-                            "kv_GBps": round(W.kv_bytes_logical([2048], 2, 128) / us / 1e3, 1)}
+                            "kv_GBps": round(W.kv_bytes_logical([2048], 2, 128) / us / 1e3, 1),
+                            "per_call_warm": time_each(dec, 1000),
+                            "per_call_cold": time_each(dec, 50, scrub),
+                            "note": "decode_us_per_call: 1000 back-to-back calls in one event window; "
+                                    "per_call_*: one event pair around each call (adds the event cost)"}
     # continuous-batching step: 64 sequences, 32 share a 2000-token prefix
     b = W.cb_step(device=device)
     P = pa.decode_partition_size(b.B, b.Hkv, b.max_context_len)
@@ -273,10 +323,16 @@ def run_context(device):
     lens = b.context_lens.cpu().numpy()
     logical = W.kv_bytes_logical(lens, 2, 128)
     unique = W.kv_bytes_unique(b.block_tables.cpu().numpy(), lens, 2, 128)
+    cold = time_each(dec3, 50, scrub)
     res["cb_step_b64"] = {"decode_us_per_call": round(us, 2), "partition_size": P,
                           "kv_logical_GBps": round(logical / us / 1e3, 1),
                           "kv_unique_GBps_warm": round(unique / us / 1e3, 1),
-                          "note": "warm: 28.5 MB of unique K/V stays in the last-level cache"}
+                          "per_call_cold": cold,
+                          "kv_unique_GBps_cold": round(unique / cold["median_us"] / 1e3, 1),
+                          "unique_frac_of_hbm_peak_cold": round(unique / cold["median_us"] / 1e3 / HBM_PEAK_GBPS, 4),
+                          "kv_unique_bytes": int(unique), "kv_logical_bytes": int(logical),
+                          "note": "warm: 28.5 MB of unique K/V stays in the last-level cache; cold: a 1 GiB "
+                                  "rewrite before each call, outside the timed window"}
     # chunked prefill: 4 x (2048 cached + 512 new), store then prefill
     b = W.chunked_prefill(device=device)
     pst = pa.prepare_cache_store(b.q, b.k, b.v, b.k_cache, b.v_cache, b.slot_mapping, b.positions,
@@ -397,8 +453,16 @@ def cpu_baseline(layers, budget_s):
                     break
             if t_total >= budget_s:
                 break
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model,
             "sample": f"fp64 numpy oracle decode of {pairs} (sequence, layer) pairs of the "
                       f"long-context workload (8192 tokens x 2 KV heads each), {t_total:.1f} s"}
 
@@ -537,6 +601,9 @@ def main():
         line["context"]["spec_verify_16x8192"] = run_verify(layers, args.steps, args.warmup)
         line["context"]["block_copies"] = run_blocks(dev)
         line["context"]["layer_ops"] = run_layer_ops(dev)
+        line["device_ceilings"] = run_ceilings(dev)
+        line["roofline"]["frac_of_measured_read"] = round(
+            line["roofline"]["achieved"] / line["device_ceilings"]["stream_read_GBps"], 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layers, args.cpu_budget)
     else:

@@ -414,6 +414,30 @@ pa_status pa_bm_swap_out(pa_block_manager* m, int64_t seq_id, int32_t* device_bl
 pa_status pa_bm_swap_in(pa_block_manager* m, int64_t seq_id, int32_t* host_blocks,
                         int32_t* device_blocks, int32_t capacity, int32_t* n);
 
+/*
+ * Device ceilings, for the rooflines of the entry points above: the pages
+ * call decode bandwidth-bound and prefill compute-bound ([T4 engine];
+ * [Pico-vLLM] "H200 comparison"), and these two kernels measure the
+ * corresponding limits of the device they run on.  Measurement only.
+ *
+ * pa_probe_stream_read: reads `bytes` (a positive multiple of 16) of device
+ * memory at buf once, with 16-byte non-temporal loads from `grid` workgroups
+ * of 256 threads, and writes the 32-bit wrap-around sum of the buffer's
+ * 32-bit words seen by workgroup w to sums[w] (sums: uint32 [grid], device
+ * memory); the grand total equals the sum of all words of the buffer mod 2^32.
+ *
+ * pa_probe_mfma_bf16: `grid` workgroups of 4 waves each run `iters` rounds of
+ * four independent 16x16x32 bf16 matrix products per wave (16384 flop each);
+ * wave v of workgroup w writes out[4*w + v] = 128 * iters exactly (out: fp32
+ * [4*grid], device memory).  flop = grid * 4 * iters * 4 * 16384.
+ *
+ * PA_ERR_NULL for a NULL pointer, PA_ERR_SHAPE for non-positive sizes or a
+ * byte count not a multiple of 16.
+ */
+pa_status pa_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sums, int32_t grid,
+                               pa_stream_t stream);
+pa_status pa_probe_mfma_bf16(int32_t iters, float* out, int32_t grid, pa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

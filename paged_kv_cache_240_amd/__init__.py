@@ -48,6 +48,8 @@ _SIGS = {
                                       _i64, _i32, _p]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_partition_size": (_i32, [_i32, _i32, _i32]),
+    "pa_probe_stream_read": (ctypes.c_int, [_p, _i64, _p, _i32, _p]),
+    "pa_probe_mfma_bf16": (ctypes.c_int, [_i32, _p, _i32, _p]),
     "pa_decode_step": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
     "pa_decode_step_partitions": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32,
@@ -679,3 +681,25 @@ class BlockManager:
         """Returns (host_blocks, device_blocks): copy host -> device with pa_swap_blocks."""
         return self._swap("pa_bm_swap_in", seq_id)
 
+
+# ---------------------------------------------------------------------------
+# Device ceilings (measurement helpers)
+# ---------------------------------------------------------------------------
+
+def prepare_probe_stream_read(buf, grid=2048, sums=None):
+    """pa_probe_stream_read over a contiguous device tensor; returns a callable whose
+    result is the per-workgroup uint32 sums (as int32) of the buffer's 32-bit words."""
+    dev = buf.device
+    if not buf.is_contiguous() or buf.numel() * buf.element_size() % 16:
+        raise ValueError("buf must be contiguous and a multiple of 16 bytes")
+    if sums is None:
+        sums = torch.empty(grid, dtype=torch.int32, device=dev)
+    return Call("pa_probe_stream_read", (_ptr(buf), buf.numel() * buf.element_size(), _ptr(sums), grid,
+                                         _stream(dev)), result=sums, keep=(buf,))
+
+
+def prepare_probe_mfma_bf16(iters, grid, device, out=None):
+    """pa_probe_mfma_bf16; returns a callable whose result is out fp32 [4 * grid]."""
+    if out is None:
+        out = torch.empty(4 * grid, dtype=torch.float32, device=device)
+    return Call("pa_probe_mfma_bf16", (int(iters), _ptr(out), int(grid), _stream(out.device)), result=out)

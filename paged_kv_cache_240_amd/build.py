@@ -25,7 +25,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 PER_FILE = {"k_cache_store.hip": ["-ffp-contract=off"]}
 SOURCES = ["pa_api.cpp", "k_cache_store.hip", "k_decode.hip", "k_decode_multi.hip", "k_prefill.hip", "k_blocks.hip",
-           "k_norm_act.hip", "block_manager.cpp"]
+           "k_norm_act.hip", "k_probe.hip", "block_manager.cpp"]
 
 
 def hipcc():

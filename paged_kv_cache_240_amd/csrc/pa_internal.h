@@ -60,4 +60,11 @@ hipError_t launch_prefill(void* out, const void* q, const void* k_cache, const v
                           const int32_t* query_start_loc, int B, int Hq, int Hkv, int D,
                           int max_blocks, int max_query_len, float scale, hipStream_t stream);
 
+// Device ceilings (measurement only): a streaming read of `bytes` (a multiple
+// of 16) writing one 32-bit sum per workgroup to sums[grid]; and `iters`
+// rounds of four bf16 MFMA chains per wave, one float per wave to out[grid*4].
+hipError_t launch_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sums, int grid,
+                                    hipStream_t stream);
+hipError_t launch_probe_mfma_bf16(int iters, float* out, int grid, hipStream_t stream);
+
 }  // namespace pa

@@ -238,3 +238,15 @@ WS16 = 2 * 12 * 8 * 129 * 4   # the pa_decode workspace at B=2, Hq=12, D=128, 12
 ])
 def test_decode_step_validation(kw, code):
     assert _step(**kw) == code
+
+
+def test_probe_validation():
+    lib = pa.load()
+    assert lib.pa_probe_stream_read(None, 16, P, 1, None) == NULL
+    assert lib.pa_probe_stream_read(P, 16, None, 1, None) == NULL
+    assert lib.pa_probe_stream_read(P, 0, P, 1, None) == SHAPE
+    assert lib.pa_probe_stream_read(P, 24, P, 1, None) == SHAPE
+    assert lib.pa_probe_stream_read(P, 16, P, 0, None) == SHAPE
+    assert lib.pa_probe_mfma_bf16(1, None, 1, None) == NULL
+    assert lib.pa_probe_mfma_bf16(0, P, 1, None) == SHAPE
+    assert lib.pa_probe_mfma_bf16(1, P, 0, None) == SHAPE
