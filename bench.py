@@ -324,6 +324,41 @@ def run_context(device):
     logical = W.kv_bytes_logical(lens, 2, 128)
     unique = W.kv_bytes_unique(b.block_tables.cpu().numpy(), lens, 2, 128)
     cold = time_each(dec3, 50, scrub)
+    # the same step with the 2000-token prefix of sequences 0-31 read once for the group
+    prefix = torch.zeros(b.B, dtype=torch.int32, device=device)
+    prefix[:32] = 2000
+    sp = pa.prepare_decode_shared_prefix(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
+                                         torch.tensor([0, 32], dtype=torch.int32, device=device), prefix,
+                                         b.scale, b.max_context_len, 32, 2000,
+                                         int((b.context_lens - prefix).max()), -1)
+    us_sp = time_calls(sp, 200)
+    cold_sp = time_each(sp, 50, scrub)
+    res["cb_step_b64_shared_prefix"] = {
+        "decode_us_per_call": round(us_sp, 2), "suffix_partition_size": "library's choice",
+        "kv_unique_GBps_warm": round(unique / us_sp / 1e3, 1),
+        "per_call_cold": cold_sp,
+        "kv_unique_GBps_cold": round(unique / cold_sp["median_us"] / 1e3, 1),
+        "unique_frac_of_hbm_peak_cold": round(unique / cold_sp["median_us"] / 1e3 / HBM_PEAK_GBPS, 4),
+        "note": "pa_decode_shared_prefix: the group's queries attend the shared prefix once "
+                "(prefix partitions on the matrix cores), suffixes by split-K, one reduce; at this "
+                "size (32 sequences, 2 MB of prefix that stays in the last-level cache) pa_decode is faster"}
+    # many sequences on one long prefix: 128 x (4096 shared + 128 own) tokens
+    lens = [4096 + 128] * 128
+    bb = W.decode_batch(lens, W.QWEN_HQ, W.QWEN_HKV, W.QWEN_D, 128 * 8 + 256 + 64, 2414, theta=1e6,
+                        shared_prefix=(list(range(128)), 256), device=device)
+    Pb = pa.decode_partition_size(bb.B, bb.Hkv, bb.max_context_len)
+    dec_b = pa.prepare_decode(bb.q, bb.k_cache, bb.v_cache, bb.block_tables, bb.context_lens, bb.scale,
+                              bb.max_context_len, Pb)
+    pre_b = torch.full((128,), 4096, dtype=torch.int32, device=device)
+    sp_b = pa.prepare_decode_shared_prefix(bb.q, bb.k_cache, bb.v_cache, bb.block_tables, bb.context_lens,
+                                           torch.tensor([0, 128], dtype=torch.int32, device=device), pre_b,
+                                           bb.scale, bb.max_context_len, 128, 4096, 128, -1)
+    uniq = W.kv_bytes_unique(bb.block_tables.cpu().numpy(), bb.context_lens.cpu().numpy(), 2, 128)
+    us_d, us_s = time_calls(dec_b, 50), time_calls(sp_b, 50)
+    res["shared_prefix_128x4096"] = {"decode_us": round(us_d, 2), "shared_prefix_us": round(us_s, 2),
+                                     "speedup": round(us_d / us_s, 2), "kv_unique_bytes": int(uniq),
+                                     "kv_logical_bytes": int(W.kv_bytes_logical(lens, 2, 128)),
+                                     "note": "pa_decode vs pa_decode_shared_prefix, warm"}
     res["cb_step_b64"] = {"decode_us_per_call": round(us, 2), "partition_size": P,
                           "kv_logical_GBps": round(logical / us / 1e3, 1),
                           "kv_unique_GBps_warm": round(unique / us / 1e3, 1),

@@ -275,6 +275,56 @@ pa_status pa_decode_step_partitions(float* o_part, float* lse, const void* q, co
                                     int32_t partition_size, pa_stream_t stream);
 
 /*
+ * Decode with shared prefixes read once ([mini-llm] §3.4: full blocks shared
+ * by several sequences, ref_count > 1; [Pico-vLLM] §3: requests sharing a
+ * system prompt).  The same result as pa_decode (up to rounding order), but
+ * the keys of a prefix shared by a group of sequences are read once for the
+ * whole group: the group's queries (every sequence and head) attend each
+ * partition of the prefix (128 to 1024 tokens, the library's choice) together
+ * on the matrix cores, each sequence's own split-K partitions cover only its
+ * tokens after the prefix, and one log-sum-exp reduce merges both sets of
+ * partials.  It pays when many sequences share a long prefix (measured: 1.6x
+ * pa_decode for 128 sequences sharing 4096 tokens); for a few sequences on a
+ * prefix that stays in the last-level cache, pa_decode is faster.
+ *
+ * group_start     int32 [num_groups + 1], device memory: group i is sequences
+ *                 group_start[i] .. group_start[i+1]-1 (contiguous, ascending,
+ *                 disjoint).  May be NULL when num_groups == 0.
+ * prefix_lens     int32 [B], device memory: the shared-prefix tokens of each
+ *                 sequence, a multiple of 16 (whole blocks), equal within a
+ *                 group, at most max_prefix and at most L_b; 0 for a sequence
+ *                 in no group (it is then decoded as by pa_decode).
+ * max_group_size  bound on group sizes (sizes the grid); max_prefix bound on
+ *                 prefix_lens, a multiple of 16, at most max_context_len.
+ * max_suffix_len  bound on L_b - prefix_lens[b] (sizes the suffix grid), at
+ *                 most max_context_len.
+ * partition_size  suffix partitions: > 0 (a multiple of 16) or -1 (library's
+ *                 choice: pa_decode's rule applied to max_suffix_len, at least
+ *                 64; the workspace query then assumes 64).
+ * workspace       pa_decode_shared_prefix_workspace_bytes(...) bytes of
+ *                 device memory: fp32 partials [B][Hq][slots][D] and
+ *                 log-sum-exps [B][Hq][slots], slots = ceil(max_suffix_len /
+ *                 P) + ceil(max_prefix / Pg) with Pg the prefix partition
+ *                 (the query assumes Pg = 128, an upper bound); a call whose
+ *                 slots cannot fit 64 with any Pg is PA_ERR_UNSUPPORTED.
+ * Device-side preconditions as for pa_decode, plus: within a group the first
+ * prefix_lens/16 block-table entries are identical (the prefix is read
+ * through the group's first sequence's table).
+ */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                               int32_t max_suffix_len, int32_t max_prefix,
+                                               int32_t partition_size);
+
+pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* group_start, const int32_t* prefix_lens, int32_t B,
+                                  int32_t num_groups, int32_t max_group_size, int32_t max_prefix,
+                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                                  int32_t max_blocks, int32_t max_context_len, int32_t max_suffix_len,
+                                  float scale, int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, pa_stream_t stream);
+
+/*
  * Copy-on-write block copies inside one pair of pools ([mini-llm] §3.4: a
  * block shared by several sequences, ref_count > 1, is copied to a freshly
  * allocated block before one of them writes it).  For every i < n, the whole

@@ -48,6 +48,10 @@ _SIGS = {
                                       _i64, _i32, _p]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_partition_size": (_i32, [_i32, _i32, _i32]),
+    "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_shared_prefix": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                               _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p,
+                                               _sz, _p]),
     "pa_probe_stream_read": (ctypes.c_int, [_p, _i64, _p, _i32, _p]),
     "pa_probe_mfma_bf16": (ctypes.c_int, [_i32, _p, _i32, _p]),
     "pa_decode_step": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
@@ -340,6 +344,53 @@ def prepare_decode_step_partitions(q, k, v, k_cache, v_cache, block_tables, cont
                  int(max_context_len), cos_sin.shape[0], float(scale), P, _stream(dev)),
                 result=(o_part, lse),
                 keep=(q, k, v, k_cache, v_cache, block_tables, context_lens, cos_sin))
+
+
+def decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, group_start, prefix_lens,
+                         scale, max_context_len, max_group_size, max_prefix, max_suffix_len=None,
+                         partition_size=-1, out=None, workspace=None):
+    """Decode with the prefixes shared by groups of sequences read once
+    (pa_decode_shared_prefix).  group_start int32 [NG+1]: group i is sequences
+    group_start[i] .. group_start[i+1]-1; prefix_lens int32 [B]: shared tokens of
+    each sequence (whole blocks, 0 outside groups); max_suffix_len bounds L_b - prefix
+    (default max_context_len).  Returns out bf16 [B, Hq, D]."""
+    return prepare_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, group_start,
+                                        prefix_lens, scale, max_context_len, max_group_size,
+                                        max_prefix, max_suffix_len, partition_size, out, workspace)()
+
+
+def prepare_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, group_start,
+                                 prefix_lens, scale, max_context_len, max_group_size, max_prefix,
+                                 max_suffix_len=None, partition_size=-1, out=None, workspace=None):
+    """Validated pa_decode_shared_prefix call (see decode_shared_prefix)."""
+    dev, B, hq, hkv, d, bs, mb = _decode_common(q, k_cache, v_cache, block_tables, context_lens)
+    _check(prefix_lens, "prefix_lens", torch.int32, 1, dev)
+    if prefix_lens.shape[0] != B:
+        raise ValueError("prefix_lens must have B entries")
+    ng = 0
+    if group_start is not None:
+        _check(group_start, "group_start", torch.int32, 1, dev)
+        ng = group_start.shape[0] - 1
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", torch.bfloat16, 3, dev)
+    if max_suffix_len is None:
+        max_suffix_len = max_context_len
+    need = int(load().pa_decode_shared_prefix_workspace_bytes(B, hq, hkv, d, int(max_suffix_len),
+                                                               int(max_prefix), int(partition_size)))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check(workspace, "workspace", workspace.dtype, None, dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return Call("pa_decode_shared_prefix",
+                (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+                 _ptr(group_start), _ptr(prefix_lens), B, ng, int(max_group_size), int(max_prefix), hq,
+                 hkv, d, bs, mb, int(max_context_len), int(max_suffix_len), float(scale),
+                 int(partition_size),
+                 _ptr(workspace), wbytes, _stream(dev)),
+                result=out, keep=(q, k_cache, v_cache, block_tables, context_lens, group_start,
+                                  prefix_lens, workspace))
 
 
 def decode_multi_workspace_bytes(B, NQ, Hq, Hkv, D, max_context_len, partition_size=-1):

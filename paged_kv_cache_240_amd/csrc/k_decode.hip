@@ -81,10 +81,14 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 // removed by selects, not arithmetic, so stale workspace contents (NaN
 // included) cannot leak.  Then: M = max lse,
 // out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M).
-template <int D, int MAXP>
+// CASC (shared-prefix decode): the row's valid slots are its
+// ceil((L - start) / part_tokens) suffix partitions, from slot 0, and the
+// ceil(start / prefix_tokens) prefix partitions, from slot slot0.
+template <int D, int MAXP, bool CASC = false>
 __device__ __forceinline__ void combine_row(uint16_t* __restrict__ out, const float* __restrict__ o_part,
                                             const float* __restrict__ lse, int L, int64_t row,
-                                            int num_parts, int part_tokens, int lane) {
+                                            int num_parts, int part_tokens, int lane, int start = 0,
+                                            int slot0 = 0, int prefix_tokens = 1) {
   constexpr int PIECES = D / 4;     // float4 pieces of one partial row
   constexpr int PPI = 64 / PIECES;  // partials covered by one wave-wide step
   constexpr int NSTEP = MAXP / PPI;
@@ -105,17 +109,19 @@ __device__ __forceinline__ void combine_row(uint16_t* __restrict__ out, const fl
     if (sub == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
     return;
   }
-  const int n = (L + part_tokens - 1) / part_tokens;
-  const float M = wave_max(lane < n ? my_lse : -INFINITY);
+  const int n = CASC ? (L - start + part_tokens - 1) / part_tokens : (L + part_tokens - 1) / part_tokens;
+  const int n_pre = CASC ? (start + prefix_tokens - 1) / prefix_tokens : 0;
+  auto valid = [&](int i) { return i < n || (CASC && i >= slot0 && i < slot0 + n_pre); };
+  const float M = wave_max(valid(lane) ? my_lse : -INFINITY);
   if (M == -INFINITY) {  // no partition saw a key of this row (multi-query rows before the cache)
     if (sub == 0) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
     return;
   }
-  const float W = wave_sum(lane < n ? exp2f(my_lse - M) : 0.f);
+  const float W = wave_sum(valid(lane) ? exp2f(my_lse - M) : 0.f);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int k = 0; k < NSTEP; ++k) {
-    const bool in = sub + PPI * k < n;
+    const bool in = valid(sub + PPI * k);
     const float w = in ? exp2f(tl[k] - M) : 0.f;
     acc.x += in ? w * t[k].x : 0.f; acc.y += in ? w * t[k].y : 0.f;
     acc.z += in ? w * t[k].z : 0.f; acc.w += in ? w * t[k].w : 0.f;
@@ -238,7 +244,8 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
               const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
               const int32_t* __restrict__ context_lens, int Hkv, int max_blocks,
               float scale_log2, int part_tokens, int num_parts, uint16_t* __restrict__ out,
-              float* __restrict__ o_part, float* __restrict__ lse, const StepArgs st) {
+              float* __restrict__ o_part, float* __restrict__ lse, const StepArgs st,
+              const int32_t* __restrict__ starts) {
   static_assert(G >= 1 && G <= 8, "query heads per KV head: 1..8");
   constexpr int KS = D / 32;    // QK k-steps over the head dimension
   constexpr int DPL = D / 16;   // PV: dims per lane = output tiles of 16 columns
@@ -263,14 +270,17 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
   const int hq0 = g * G;
   const int32_t* bt_row = block_tables + (int64_t)b * max_blocks;
   const int L = context_lens[b];
+  // split-K with starts: sequence b's partitions cover [starts[b], L) (a
+  // shared prefix before it is attended elsewhere); starts[b] is whole blocks
+  const int start = (SPLIT && starts != nullptr) ? starts[b] : 0;
   // The first chunk's table entries are requested before L is known (indices
   // clamped into the table; an entry past the sequence is never dereferenced:
   // it is replaced by the range's first block once L arrives), so the first
   // K/V loads wait for one round trip instead of two.
-  const int lb0 = SPLIT ? p * part_tokens / kBlockSize : 0;
+  const int lb0 = SPLIT ? (start + p * part_tokens) / kBlockSize : 0;
   const int lb_spec = lb0 + wave + kWaves * (threadIdx.x & 7);
   const int ent_spec = bt_row[min(lb_spec, max_blocks - 1)];
-  const int ent_first = bt_row[lb0];
+  const int ent_first = bt_row[min(lb0, max_blocks - 1)];  // lb0 may lie past a short suffix
   const int col = lane & 15, quad = lane >> 4;  // MFMA lane roles
   // B operand of QK: query row of head `col` (zero beyond G), 8 dims per
   // k-step; padding lanes read head 0 and discard it (a select, not a branch)
@@ -284,7 +294,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
 
   int t_begin = 0, t_end = L;
   if (SPLIT) {
-    t_begin = p * part_tokens;
+    t_begin = start + p * part_tokens;
     if (t_begin >= L) return;  // empty partition: not written, not combined
     t_end = min(t_begin + part_tokens, L);
   } else if (L <= 0) {
@@ -302,8 +312,8 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
   // slot when r_new is 0.  The loads and the cos/sin row are requested here,
   // before the ring fill, and consumed after it.
   const int nb_new = (L - 1) / kBlockSize, r_new = (L - 1) % kBlockSize;
-  const int lb_new = nb_new - (SPLIT ? p * part_tokens / kBlockSize : 0);  // in this range
-  const bool own_wg = FUSED && (!SPLIT || p == (L - 1) / part_tokens);
+  const int lb_new = nb_new - lb0;  // in this range
+  const bool own_wg = FUSED && (!SPLIT || p == (L - 1 - start) / part_tokens);
   const bool owner = own_wg && wave == lb_new % kWaves;
   const int c_new = lb_new / kChunkBlocks, i_new = (lb_new % kChunkBlocks) / kWaves;
   float cs_c[KS / 2][8], cs_s[KS / 2][8];
@@ -620,6 +630,18 @@ combine_kernel(uint16_t* __restrict__ out, const float* __restrict__ o_part,
                        part_tokens, threadIdx.x);
 }
 
+// Shared-prefix decode: suffix and prefix partials of each row.
+template <int D, int MAXP>
+__global__ void __launch_bounds__(64)
+combine_cascade_kernel(uint16_t* __restrict__ out, const float* __restrict__ o_part,
+                       const float* __restrict__ lse, const int32_t* __restrict__ context_lens,
+                       const int32_t* __restrict__ starts, int Hq, int num_slots, int part_tokens,
+                       int slot0, int prefix_tokens) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  combine_row<D, MAXP, true>(out, o_part, lse, context_lens[b], (int64_t)b * Hq + h, num_slots,
+                             part_tokens, threadIdx.x, starts[b], slot0, prefix_tokens);
+}
+
 template <int D>
 __global__ void __launch_bounds__(64)
 combine_many_kernel(uint16_t* __restrict__ out, const float* __restrict__ o_part,
@@ -634,7 +656,8 @@ template <int D, int G, bool FUSED>
 hipError_t launch_dg(void* out, float* o_part, float* lse, const void* q, const void* k_cache,
                      const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
                      int B, int Hkv, int max_blocks, int max_context_len, float scale,
-                     int partition_size, const StepArgs& st, hipStream_t stream) {
+                     int partition_size, const StepArgs& st, const int32_t* starts,
+                     hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kc = static_cast<const uint16_t*>(k_cache);
@@ -645,15 +668,15 @@ hipError_t launch_dg(void* out, float* o_part, float* lse, const void* q, const 
     if (partition_size <= kChunkTokens)
       hipLaunchKernelGGL((decode_kernel<D, G, true, true, FUSED>), dim3(np, Hkv, B), dim3(256), 0,
                          stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks,
-                         scale_log2, partition_size, np, oo, o_part, lse, st);
+                         scale_log2, partition_size, np, oo, o_part, lse, st, starts);
     else
       hipLaunchKernelGGL((decode_kernel<D, G, true, false, FUSED>), dim3(np, Hkv, B), dim3(256), 0,
                          stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks,
-                         scale_log2, partition_size, np, oo, o_part, lse, st);
+                         scale_log2, partition_size, np, oo, o_part, lse, st, starts);
   } else {
     hipLaunchKernelGGL((decode_kernel<D, G, false, false, FUSED>), dim3(1, Hkv, B), dim3(256), 0,
                        stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks, scale_log2,
-                       0, 1, oo, o_part, lse, st);
+                       0, 1, oo, o_part, lse, st, nullptr);
   }
   return hipGetLastError();
 }
@@ -661,8 +684,9 @@ hipError_t launch_dg(void* out, float* o_part, float* lse, const void* q, const 
 template <int D, bool FUSED>
 hipError_t launch_d(int G, void* out, float* o_part, float* lse, const void* q, const void* k_cache,
                     const void* v_cache, const int32_t* bt, const int32_t* cl, int B, int Hkv,
-                    int mb, int mcl, float scale, int ps, const StepArgs& sa, hipStream_t st) {
-#define PA_DG(GG) return launch_dg<D, GG, FUSED>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, Hkv, mb, mcl, scale, ps, sa, st)
+                    int mb, int mcl, float scale, int ps, const StepArgs& sa, const int32_t* starts,
+                    hipStream_t st) {
+#define PA_DG(GG) return launch_dg<D, GG, FUSED>(out, o_part, lse, q, k_cache, v_cache, bt, cl, B, Hkv, mb, mcl, scale, ps, sa, starts, st)
   switch (G) {
     case 1: PA_DG(1);
     case 2: PA_DG(2);
@@ -689,9 +713,10 @@ hipError_t launch_decode(void* out, float* o_part, float* lse, const void* q, co
   if (D == 128)
     return launch_d<128, false>(G, out, o_part, lse, q, k_cache, v_cache, block_tables, context_lens,
                                 B, Hkv, max_blocks, max_context_len, scale, partition_size, none,
-                                stream);
+                                nullptr, stream);
   return launch_d<64, false>(G, out, o_part, lse, q, k_cache, v_cache, block_tables, context_lens, B,
-                             Hkv, max_blocks, max_context_len, scale, partition_size, none, stream);
+                             Hkv, max_blocks, max_context_len, scale, partition_size, none, nullptr,
+                             stream);
 }
 
 // The decode step with the store folded into the decode kernel: RoPE of q and
@@ -708,12 +733,78 @@ hipError_t launch_decode_step(void* out, float* o_part, float* lse, const void* 
   const StepArgs sa{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), cos_sin};
   const hipError_t e =
       D == 128 ? launch_d<128, true>(G, out, o_part, lse, q, k_cache, v_cache, block_tables, context_lens,
-                                     B, Hkv, max_blocks, max_context_len, scale, partition_size, sa, stream)
+                                     B, Hkv, max_blocks, max_context_len, scale, partition_size, sa, nullptr, stream)
                : launch_d<64, true>(G, out, o_part, lse, q, k_cache, v_cache, block_tables, context_lens,
-                                    B, Hkv, max_blocks, max_context_len, scale, partition_size, sa, stream);
+                                    B, Hkv, max_blocks, max_context_len, scale, partition_size, sa, nullptr, stream);
   if (e != hipSuccess || partition_size <= 0 || !with_combine) return e;
   const int np = (max_context_len + partition_size - 1) / partition_size;
   return launch_decode_combine(out, o_part, lse, context_lens, B, Hkv * G, D, np, partition_size, stream);
+}
+
+// Split-K partitions of each sequence's suffix [starts[b], L_b).
+hipError_t launch_decode_suffix(float* o_part, float* lse, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* starts, int B, int Hq,
+                                int Hkv, int D, int max_blocks, int max_context_len, float scale,
+                                int partition_size, int num_slots, hipStream_t stream) {
+  // the partials' row stride is num_slots, so the kernel's num_parts is num_slots
+  const int G = Hq / Hkv;
+  const StepArgs none{};
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const int np = (max_context_len + partition_size - 1) / partition_size;
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const auto* kc = static_cast<const uint16_t*>(k_cache);
+  const auto* vc = static_cast<const uint16_t*>(v_cache);
+#define PA_SUF(DD, GG)                                                                             \
+  do {                                                                                             \
+    if (partition_size <= kChunkTokens)                                                            \
+      hipLaunchKernelGGL((decode_kernel<DD, GG, true, true, false>), dim3(np, Hkv, B), dim3(256), 0, \
+                         stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks,           \
+                         scale_log2, partition_size, num_slots, nullptr, o_part, lse, none, starts); \
+    else                                                                                           \
+      hipLaunchKernelGGL((decode_kernel<DD, GG, true, false, false>), dim3(np, Hkv, B), dim3(256), 0, \
+                         stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks,           \
+                         scale_log2, partition_size, num_slots, nullptr, o_part, lse, none, starts); \
+  } while (0)
+#define PA_SUF_G(DD)                 \
+  switch (G) {                       \
+    case 1: PA_SUF(DD, 1); break;    \
+    case 2: PA_SUF(DD, 2); break;    \
+    case 3: PA_SUF(DD, 3); break;    \
+    case 4: PA_SUF(DD, 4); break;    \
+    case 5: PA_SUF(DD, 5); break;    \
+    case 6: PA_SUF(DD, 6); break;    \
+    case 7: PA_SUF(DD, 7); break;    \
+    case 8: PA_SUF(DD, 8); break;    \
+    default: return hipErrorInvalidValue; \
+  }
+  if (D == 128) { PA_SUF_G(128) } else { PA_SUF_G(64) }
+#undef PA_SUF_G
+#undef PA_SUF
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine_cascade(void* out, const float* o_part, const float* lse,
+                                         const int32_t* context_lens, const int32_t* starts, int B,
+                                         int Hq, int D, int num_slots, int partition_size,
+                                         int slot0, int prefix_tokens, hipStream_t stream) {
+  auto* oo = static_cast<uint16_t*>(out);
+  const dim3 grid(Hq, B), block(64);
+#define PA_CC(DD, MP)                                                                          \
+  hipLaunchKernelGGL((combine_cascade_kernel<DD, MP>), grid, block, 0, stream, oo, o_part, lse,  \
+                     context_lens, starts, Hq, num_slots, partition_size, slot0, prefix_tokens)
+  if (num_slots > 64) return hipErrorInvalidValue;
+  if (D == 128) {
+    if (num_slots <= 16) PA_CC(128, 16);
+    else if (num_slots <= 32) PA_CC(128, 32);
+    else PA_CC(128, 64);
+  } else {
+    if (num_slots <= 16) PA_CC(64, 16);
+    else if (num_slots <= 32) PA_CC(64, 32);
+    else PA_CC(64, 64);
+  }
+#undef PA_CC
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_combine(void* out, const float* o_part, const float* lse,

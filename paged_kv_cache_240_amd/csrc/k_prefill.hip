@@ -71,13 +71,32 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-template <int D, int G>
+// Shared-prefix mode (PART): a group of decode sequences sharing their first
+// blocks.  Group gi is sequences group_start[gi] .. group_start[gi+1]-1, all
+// with the same first prefix_lens[group_start[gi]] tokens (whole blocks, read
+// through the first sequence's table).  Workgroup (rb, g, gi*parts + kp)
+// takes rows (sequence s of the group, head h) r = s*G + h, and keys
+// [kp*part_tokens, min((kp+1)*part_tokens, prefix)) with no causal mask, and
+// writes the normalised fp32 partial and its base-2 log-sum-exp to slot
+// slot0 + kp of each row, in the split-K workspace layout.
+struct GroupArgs {
+  const int32_t* group_start;
+  const int32_t* prefix_lens;
+  int part_tokens;  // multiple of kStepKeys
+  int parts;        // partitions per group (grid z = groups * parts)
+  int slot0;        // first workspace slot of the prefix partitions
+  int num_slots;    // slots per row in the workspace
+  float* o_part;    // [B][Hq][num_slots][D]
+  float* lse;       // [B][Hq][num_slots]
+};
+
+template <int D, int G, bool PART>
 __global__ void __launch_bounds__(kThreads)
 prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
                const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
                const int32_t* __restrict__ query_start_loc, int Hkv, int max_blocks,
-               float scale_log2) {
+               float scale_log2, const GroupArgs ga) {
   constexpr int NCH = D / 8;         // 16-byte chunks per row
   constexpr int KS = D / 32;         // MFMA k-steps over the head dimension
   constexpr int DT = D / 16;         // 16-dim output tiles
@@ -102,21 +121,40 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   const int rb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int Hq = Hkv * G;
 
-  const int q0 = query_start_loc[b];
-  const int C = query_start_loc[b + 1] - q0;
-  const int L = context_lens[b];
+  // Chunked prefill: rows of sequence b's chunk, keys [0, kmax) under the
+  // causal limits.  Shared prefix: rows of group gi, keys [kbeg, L) where L
+  // is the partition's end (keys past it are treated as past the sequence).
+  int q0, C, L, kbeg = 0, kp = 0;
+  int32_t seq_first;  // sequence whose table is read
+  if constexpr (PART) {
+    const int gi = b / ga.parts;
+    kp = b % ga.parts;
+    q0 = ga.group_start[gi];
+    C = ga.group_start[gi + 1] - q0;  // sequences of the group
+    const int pre = ga.prefix_lens[q0];
+    kbeg = kp * ga.part_tokens;
+    if (kbeg >= pre) return;
+    L = min(kbeg + ga.part_tokens, pre);
+    seq_first = q0;
+  } else {
+    q0 = query_start_loc[b];
+    C = query_start_loc[b + 1] - q0;
+    L = context_lens[b];
+    seq_first = b;
+  }
   const int nrows = C * G;
   const int row0_wg = rb * kRowsPerWG;
   if (row0_wg >= nrows) return;
   const int pos_last = min(nrows, row0_wg + kRowsPerWG) - 1;  // last valid row of the WG
   // keys any row of this workgroup can see: up to position L - C + pos_max
-  const int kmax = min(L, L - C + pos_last / G + 1);
-  const int ntiles = (kmax + kStepKeys - 1) / kStepKeys;
+  const int kmax = PART ? L : min(L, L - C + pos_last / G + 1);
+  const int tbase = kbeg / kStepKeys;
+  const int ntiles = (kmax - kbeg + kStepKeys - 1) / kStepKeys;
   const int nsteps = (ntiles + 1) / 2;                 // tiles of half 0 (half 1 has <= as many)
-  const int tile0 = half * nsteps;                     // first tile of this wave's half
-  const int tile_end = half == 0 ? nsteps : ntiles;    // one past its last tile
+  const int tile0 = tbase + half * nsteps;             // first tile of this wave's half
+  const int tile_end = tbase + (half == 0 ? nsteps : ntiles);  // one past its last tile
   const int nblk_seq = (L + kBlockSize - 1) / kBlockSize;
-  const int32_t* bt_row = block_tables + (int64_t)b * max_blocks;
+  const int32_t* bt_row = block_tables + (int64_t)seq_first * max_blocks;
   const int64_t head_off = (int64_t)g * kBlockSize * D;
   const int64_t blk_stride = (int64_t)Hkv * kBlockSize * D;
 
@@ -130,7 +168,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     rvalid[rt] = r < nrows;
     const int pos = rvalid[rt] ? r / G : 0;
     const int h = rvalid[rt] ? r % G : 0;
-    lim[rt] = rvalid[rt] ? L - C + pos : L - 1;
+    lim[rt] = PART ? L - 1 : rvalid[rt] ? L - C + pos : L - 1;
     const uint16_t* qrow = q + ((int64_t)(q0 + pos) * Hq + g * G + h) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -140,7 +178,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     }
   }
   // smallest causal limit over the workgroup's rows (tiles past it need masks)
-  const int lim_min_wg = L - C + row0_wg / G;
+  const int lim_min_wg = PART ? L - 1 : L - C + row0_wg / G;
 
   // ---- staging: global -> registers -> LDS ----------------------------------------
   // A step is kStepBlocks blocks.  Every load is unconditional, from an
@@ -355,10 +393,27 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const float M = fmaxf(m0, m1);
     const float w0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m0 - M) * scale_log2);
     const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - M) * scale_log2);
-    const float inv = 1.f / (w0 * l0 + w1 * l1);
+    const float lsum = w0 * l0 + w1 * l1;
+    const float inv = 1.f / lsum;
     if (!rvalid[rt]) continue;
     const int r = row0_wg + hw * kRowsPerWave + rt * 16 + col;
     const int pos = r / G, h = r % G;
+    if constexpr (PART) {
+      // partial of row (sequence q0 + pos, head g*G + h) at slot slot0 + kp
+      const int64_t slot = ((int64_t)(q0 + pos) * Hq + g * G + h) * ga.num_slots + ga.slot0 + kp;
+      float* orow = ga.o_part + slot * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        float4 y;
+        y.x = (w0 * o[dt][rt][0] + w1 * mg_at(rt, dt * 4 + 0)) * inv;
+        y.y = (w0 * o[dt][rt][1] + w1 * mg_at(rt, dt * 4 + 1)) * inv;
+        y.z = (w0 * o[dt][rt][2] + w1 * mg_at(rt, dt * 4 + 2)) * inv;
+        y.w = (w0 * o[dt][rt][3] + w1 * mg_at(rt, dt * 4 + 3)) * inv;
+        *reinterpret_cast<float4*>(orow + dt * 16 + quad * 4) = y;
+      }
+      if (quad == 0) ga.lse[slot] = M * scale_log2 + log2f(lsum);
+      continue;
+    }
     uint16_t* orow = out + ((int64_t)(q0 + pos) * Hq + g * G + h) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -371,13 +426,13 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   }
 }
 
-template <int D>
+template <int D, bool PART>
 hipError_t launch_d(int G, dim3 grid, hipStream_t stream, uint16_t* out, const uint16_t* q,
                     const uint16_t* kc, const uint16_t* vc, const int32_t* bt, const int32_t* cl,
-                    const int32_t* qsl, int Hkv, int mb, float sl) {
+                    const int32_t* qsl, int Hkv, int mb, float sl, const GroupArgs& ga) {
 #define PA_PREFILL(GG)                                                                        \
-  hipLaunchKernelGGL((prefill_kernel<D, GG>), grid, dim3(kThreads), 0, stream, out, q, kc, vc, bt,  \
-                     cl, qsl, Hkv, mb, sl)
+  hipLaunchKernelGGL((prefill_kernel<D, GG, PART>), grid, dim3(kThreads), 0, stream, out, q, kc, vc, \
+                     bt, cl, qsl, Hkv, mb, sl, ga)
   switch (G) {
     case 1: PA_PREFILL(1); break;
     case 2: PA_PREFILL(2); break;
@@ -407,11 +462,36 @@ hipError_t launch_prefill(void* out, const void* q, const void* k_cache, const v
   auto* qq = static_cast<const uint16_t*>(q);
   auto* kc = static_cast<const uint16_t*>(k_cache);
   auto* vc = static_cast<const uint16_t*>(v_cache);
+  const GroupArgs none{};
   if (D == 128)
-    return launch_d<128>(G, grid, stream, o, qq, kc, vc, block_tables, context_lens,
-                         query_start_loc, Hkv, max_blocks, sl);
-  return launch_d<64>(G, grid, stream, o, qq, kc, vc, block_tables, context_lens, query_start_loc,
-                      Hkv, max_blocks, sl);
+    return launch_d<128, false>(G, grid, stream, o, qq, kc, vc, block_tables, context_lens,
+                                query_start_loc, Hkv, max_blocks, sl, none);
+  return launch_d<64, false>(G, grid, stream, o, qq, kc, vc, block_tables, context_lens,
+                             query_start_loc, Hkv, max_blocks, sl, none);
+}
+
+// Shared-prefix partials of decode queries: grid (row blocks, Hkv, groups * parts).
+hipError_t launch_group_prefix(float* o_part, float* lse, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* group_start, const int32_t* prefix_lens, int groups,
+                               int max_group_size, int max_prefix, int part_tokens, int slot0,
+                               int num_slots, int Hq, int Hkv, int D, int max_blocks, float scale,
+                               hipStream_t stream) {
+  const int G = Hq / Hkv;
+  const int parts = (max_prefix + part_tokens - 1) / part_tokens;
+  const int rblocks = (max_group_size * G + kRowsPerWG - 1) / kRowsPerWG;
+  if (groups <= 0 || parts <= 0 || rblocks <= 0) return hipSuccess;
+  const dim3 grid(rblocks, Hkv, groups * parts);
+  const GroupArgs ga{group_start, prefix_lens, part_tokens, parts, slot0, num_slots, o_part, lse};
+  const float sl = scale * 1.4426950408889634f;
+  auto* qq = static_cast<const uint16_t*>(q);
+  auto* kc = static_cast<const uint16_t*>(k_cache);
+  auto* vc = static_cast<const uint16_t*>(v_cache);
+  if (D == 128)
+    return launch_d<128, true>(G, grid, stream, nullptr, qq, kc, vc, block_tables, nullptr, nullptr,
+                               Hkv, max_blocks, sl, ga);
+  return launch_d<64, true>(G, grid, stream, nullptr, qq, kc, vc, block_tables, nullptr, nullptr, Hkv,
+                            max_blocks, sl, ga);
 }
 
 }  // namespace pa

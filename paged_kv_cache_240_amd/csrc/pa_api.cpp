@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "../../include/pa.h"
@@ -244,6 +245,107 @@ pa_status pa_decode_step_partitions(float* o_part, float* lse, const void* q, co
                                          block_tables, context_lens, cos_sin, B, Hq, Hkv, D,
                                          max_blocks, max_context_len, scale, partition_size, false,
                                          static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+constexpr int kPrefixPartTokens = 128;  // smallest shared-prefix partition: a key tile per half
+constexpr int kMaxCascadeSlots = 64;
+
+int32_t cascade_slots(int32_t max_suffix, int32_t P, int32_t max_prefix, int32_t Pg = kPrefixPartTokens) {
+  return (int32_t)(ceil_div(max_suffix, P) + ceil_div(max_prefix, Pg));
+}
+
+// Prefix partition size: each group workgroup costs a fixed latency (about 8
+// us: its loads, one LDS stage, the merge of its halves) plus about 3 us per
+// 128 keys, and workgroups beyond one per CU run in further rounds; take the
+// size with the least estimated time whose slots fit.
+int32_t prefix_partition(int32_t row_blocks, int32_t max_prefix, int32_t suffix_slots) {
+  const int cus = device_cu_count();
+  int32_t best = 0;
+  double best_t = 1e30;
+  for (int32_t Pg = kPrefixPartTokens; Pg <= 8 * kPrefixPartTokens; Pg *= 2) {
+    if (suffix_slots + ceil_div(max_prefix, Pg) > kMaxCascadeSlots) continue;
+    const int64_t wgs = (int64_t)row_blocks * ceil_div(max_prefix, Pg);
+    const double t = (double)ceil_div(wgs, cus) * (8.0 + 3.0 * Pg / kPrefixPartTokens);
+    if (t < best_t) {
+      best_t = t;
+      best = Pg;
+    }
+  }
+  return best;
+}
+}  // namespace
+
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                               int32_t max_suffix_len, int32_t max_prefix,
+                                               int32_t partition_size) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_suffix_len < 0 || max_prefix < 0) return 0;
+  // -1: the smallest partition the library may choose, so the most slots
+  const int32_t P = partition_size == -1 ? 64 : partition_size;
+  if (P <= 0 || P % 16 != 0) return 0;
+  const int64_t slots = cascade_slots(std::max(max_suffix_len, 1), P, max_prefix);
+  return (size_t)((int64_t)B * Hq * slots * (D + 1) * (int64_t)sizeof(float));
+}
+
+pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* group_start, const int32_t* prefix_lens, int32_t B,
+                                  int32_t num_groups, int32_t max_group_size, int32_t max_prefix,
+                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                                  int32_t max_blocks, int32_t max_context_len, int32_t max_suffix_len,
+                                  float scale, int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, pa_stream_t stream) {
+  if (!out || !prefix_lens || (num_groups > 0 && !group_start)) return PA_ERR_NULL;
+  pa_status st = check_decode(q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, D,
+                              block_size, max_blocks, max_context_len);
+  if (st != PA_OK) return st;
+  if (num_groups < 0 || max_prefix < 0 || max_prefix % 16 != 0 || max_prefix > max_context_len ||
+      max_suffix_len < 0 || max_suffix_len > max_context_len)
+    return PA_ERR_SHAPE;
+  if (num_groups > 0 && (max_group_size <= 0 || max_group_size > B)) return PA_ERR_SHAPE;
+  if (partition_size < -1 || partition_size == 0 || (partition_size > 0 && partition_size % 16 != 0))
+    return PA_ERR_SHAPE;
+  if (B == 0 || max_context_len == 0) return B == 0 ? PA_OK : from_hip(pa::launch_decode(
+      out, nullptr, nullptr, q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, D,
+      max_blocks, max_context_len, scale, 0, static_cast<hipStream_t>(stream)));
+  const int32_t suf = std::max(max_suffix_len, 1);
+  // the library's choice for the suffixes: pa_decode's rule on the suffix length
+  // (about two workgroups per CU), at least 64 tokens, one partition when the
+  // batch alone fills the device
+  int32_t P = partition_size;
+  if (P == -1) {
+    P = pa_decode_partition_size(B, Hkv, suf);
+    P = P == 0 ? (int32_t)(ceil_div(suf, 16) * 16) : P;
+    P = std::max<int32_t>(P, 64);
+  }
+  const int32_t suffix_slots = (int32_t)ceil_div(suf, P);
+  // row blocks of 128 (sequence, head) rows per group, times KV heads and groups
+  const int32_t row_blocks = (int32_t)(ceil_div((int64_t)std::max(max_group_size, 1) * (Hq / Hkv), 128) *
+                                       Hkv * std::max(num_groups, 1));
+  const int32_t Pg = max_prefix > 0 ? prefix_partition(row_blocks, max_prefix, suffix_slots)
+                                    : kPrefixPartTokens;
+  if (Pg == 0) return PA_ERR_UNSUPPORTED;
+  const int32_t slots = cascade_slots(suf, P, max_prefix, Pg);
+  if (slots > kMaxCascadeSlots) return PA_ERR_UNSUPPORTED;
+  // the workspace query sizes for the smallest prefix partition: always enough
+  const size_t need = (size_t)((int64_t)B * Hq * slots * (D + 1) * (int64_t)sizeof(float));
+  if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* o_part = static_cast<float*>(workspace);
+  float* lse = o_part + (int64_t)B * Hq * slots * D;
+  const int32_t slot0 = suffix_slots;
+  if (num_groups > 0 && max_prefix > 0) {
+    hipError_t e = pa::launch_group_prefix(o_part, lse, q, k_cache, v_cache, block_tables, group_start,
+                                           prefix_lens, num_groups, max_group_size, max_prefix,
+                                           Pg, slot0, slots, Hq, Hkv, D, max_blocks, scale, s);
+    if (e != hipSuccess) return PA_ERR_HIP;
+  }
+  hipError_t e = pa::launch_decode_suffix(o_part, lse, q, k_cache, v_cache, block_tables,
+                                          context_lens, prefix_lens, B, Hq, Hkv, D, max_blocks,
+                                          suf, scale, P, slots, s);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  return from_hip(pa::launch_decode_combine_cascade(out, o_part, lse, context_lens, prefix_lens, B,
+                                                    Hq, D, slots, P, slot0, Pg, s));
 }
 
 size_t pa_decode_multi_workspace_bytes(int32_t B, int32_t NQ, int32_t Hq, int32_t Hkv, int32_t D,

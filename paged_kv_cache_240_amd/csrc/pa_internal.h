@@ -67,4 +67,24 @@ hipError_t launch_probe_stream_read(const void* buf, int64_t bytes, uint32_t* su
                                     hipStream_t stream);
 hipError_t launch_probe_mfma_bf16(int iters, float* out, int grid, hipStream_t stream);
 
+// Shared-prefix decode: the group prefixes' partials (prefill kernel, group
+// mode), the suffix partitions of each sequence from starts[b], and their
+// log-sum-exp reduce.  Workspace rows hold num_slots partials: suffix
+// partitions from slot 0, prefix partitions from slot0.
+hipError_t launch_group_prefix(float* o_part, float* lse, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* group_start, const int32_t* prefix_lens, int groups,
+                               int max_group_size, int max_prefix, int part_tokens, int slot0,
+                               int num_slots, int Hq, int Hkv, int D, int max_blocks, float scale,
+                               hipStream_t stream);
+hipError_t launch_decode_suffix(float* o_part, float* lse, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* starts, int B, int Hq,
+                                int Hkv, int D, int max_blocks, int max_context_len, float scale,
+                                int partition_size, int num_slots, hipStream_t stream);
+hipError_t launch_decode_combine_cascade(void* out, const float* o_part, const float* lse,
+                                         const int32_t* context_lens, const int32_t* starts, int B,
+                                         int Hq, int D, int num_slots, int partition_size,
+                                         int slot0, int prefix_tokens, hipStream_t stream);
+
 }  // namespace pa

@@ -250,3 +250,34 @@ def test_probe_validation():
     assert lib.pa_probe_mfma_bf16(1, None, 1, None) == NULL
     assert lib.pa_probe_mfma_bf16(0, P, 1, None) == SHAPE
     assert lib.pa_probe_mfma_bf16(1, P, 0, None) == SHAPE
+
+
+def _sp(**kw):
+    a = dict(out=P, q=P, kc=P, vc=P, bt=P, cl=P, gs=P, pl=P, B=4, ng=1, mg=4, mp=32, Hq=12, Hkv=2,
+             D=128, bs=16, mb=8, mcl=128, ms=128, scale=0.088, ps=64, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return pa.load().pa_decode_shared_prefix(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"],
+                                             a["gs"], a["pl"], a["B"], a["ng"], a["mg"], a["mp"],
+                                             a["Hq"], a["Hkv"], a["D"], a["bs"], a["mb"], a["mcl"],
+                                             a["ms"], a["scale"], a["ps"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), NULL), (dict(pl=None), NULL), (dict(gs=None), NULL), (dict(q=None), NULL),
+    (dict(ng=-1), SHAPE), (dict(mp=-16), SHAPE), (dict(mp=24), SHAPE), (dict(mp=144), SHAPE),
+    (dict(mg=0), SHAPE), (dict(mg=5), SHAPE), (dict(ps=0), SHAPE), (dict(ps=24), SHAPE),
+    (dict(ms=-1), SHAPE), (dict(ms=129), SHAPE),
+    (dict(ws=None), WS), (dict(wsb=100), WS), (dict(ps=16, mcl=1024, ms=1024, mp=128, mb=64), UNSUP),
+    (dict(D=80), UNSUP), (dict(B=0, ng=0), OK),
+])
+def test_shared_prefix_validation(kw, code):
+    assert _sp(**kw) == code
+
+
+def test_shared_prefix_workspace_size():
+    lib = pa.load()
+    # slots = ceil(max_suffix_len / P) + ceil(max_prefix / 128)
+    assert lib.pa_decode_shared_prefix_workspace_bytes(64, 12, 2, 128, 1024, 2000, 512) == \
+        64 * 12 * (2 + 16) * 129 * 4
+    assert lib.pa_decode_shared_prefix_workspace_bytes(4, 12, 2, 128, 128, 0, 64) == 4 * 12 * 2 * 129 * 4
+    assert lib.pa_decode_shared_prefix_workspace_bytes(4, 12, 2, 128, 128, 0, 24) == 0
