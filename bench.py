@@ -197,6 +197,32 @@ def run_long(layers, steps, warmup):
             "partition_us": window(kernel_only) * 1000 / len(L)}
 
 
+def run_graph(layers, steps, warmup):
+    """The same 28-layer decode step captured once in a HIP graph and replayed
+    (what a serving loop does to spare the per-launch host cost)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for b in layers:
+            b.meta["step_partitions"](s)
+            b.meta["step_combine"](s)
+    _sync()
+    for _ in range(warmup):
+        g.replay()
+    _sync()
+    t0, t1 = _event(), _event()
+    t0.record()
+    for _ in range(steps):
+        g.replay()
+    t1.record()
+    _sync()
+    ms = t0.elapsed_time(t1) / steps
+    kv = sum(W.kv_bytes_logical(b.context_lens.cpu().numpy(), b.Hkv, b.D) for b in layers)
+    return {"us_per_layer": round(ms * 1000 / len(layers), 2), "kv_GBps": round(kv / (ms * 1e-3) / 1e9, 1),
+            "note": "pa_decode_step's two launches per layer, 28 layers, captured once and replayed"}
+
+
 def run_verify(layers, steps, warmup, nq=5):
     """Speculative verification over the same 28 layer caches: nq queries per
     sequence (the last accepted token and nq-1 drafts) through pa_decode_multi
@@ -633,6 +659,7 @@ def main():
     }
     if not args.no_context:
         line["context"] = run_context(dev)
+        line["context"]["decode_step_graph"] = run_graph(layers, args.steps, args.warmup)
         line["context"]["spec_verify_16x8192"] = run_verify(layers, args.steps, args.warmup)
         line["context"]["block_copies"] = run_blocks(dev)
         line["context"]["layer_ops"] = run_layer_ops(dev)

@@ -121,6 +121,8 @@ class Call:
     Calling the object enqueues the operation again with the same pointers,
     sizes and stream (no per-call Python checks), e.g. once per decode step
     while the tensors stay in place.  `result` is what the call writes.
+    call(stream) enqueues on another torch stream instead (every entry point
+    takes its stream last), e.g. the capture stream of a HIP graph.
     """
 
     __slots__ = ("name", "fn", "args", "result", "keep")
@@ -132,8 +134,11 @@ class Call:
         self.result = result
         self.keep = keep  # the tensors whose pointers are in args stay alive with the call
 
-    def __call__(self):
-        st = self.fn(*self.args)
+    def __call__(self, stream=None):
+        args = self.args
+        if stream is not None:
+            args = args[:-1] + (ctypes.c_void_p(stream.cuda_stream),)
+        st = self.fn(*args)
         if st != 0:
             raise PAError(self.name, st)
         return self.result
