@@ -108,8 +108,12 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
 
 /*
  * The partition size pa_decode uses when asked to choose (partition_size
- * -1): 0 (single pass) when B * Hkv alone fills the GPU, otherwise a multiple
- * of 16.  Host-only; reads the device's compute-unit count once.
+ * -1): 0 (single pass) when B * Hkv alone fills the GPU twice over or the
+ * contexts are at most 512 tokens; up to 4096 tokens, 256 (128 when the batch
+ * would not give every compute unit a workgroup); longer, 512; doubled up to
+ * 512 while the grid would exceed two workgroups per compute unit, and beyond
+ * while a sequence would need more than 64 partitions.  Host-only; reads the
+ * device's compute-unit count once.
  */
 int32_t pa_decode_partition_size(int32_t B, int32_t Hkv, int32_t max_context_len);
 

@@ -117,15 +117,27 @@ pa_status pa_cache_store(void* q, const void* k, const void* v, void* k_cache, v
 }
 
 int32_t pa_decode_partition_size(int32_t B, int32_t Hkv, int32_t max_context_len) {
+  // Measured on MI355X (Qwen head shape): a partition costs a fixed latency
+  // (table, K/V and partial round trips) and the reduce is a launch of its
+  // own, cheap up to 64 partitions per sequence; so
+  //  * a batch that fills the device twice over, or contexts up to 512
+  //    tokens: one pass, no reduce;
+  //  * up to 4096 tokens: 256-token partitions, 128 when the batch would not
+  //    give every CU a workgroup;
+  //  * longer: 512-token partitions;
+  //  * doubled up to 512 while the grid would not be resident at once (two
+  //    workgroups per CU), and beyond while a sequence needs more than 64.
   if (B <= 0 || Hkv <= 0 || max_context_len <= 0) return 0;
-  const int64_t target = 2LL * device_cu_count();  // workgroups to fill the GPU twice over
+  const int64_t cus = device_cu_count();
   const int64_t pairs = (int64_t)B * Hkv;
-  if (pairs >= target) return 0;
-  const int64_t parts = ceil_div(target, pairs);
-  int64_t P = ceil_div(ceil_div(max_context_len, parts), 16) * 16;
-  if (P < 64) P = 64;
-  if (P > 512) P = 512;
-  if (P >= max_context_len) return 0;
+  if (pairs >= 2 * cus || max_context_len <= 512) return 0;
+  int64_t P;
+  if (max_context_len <= 4096)
+    P = pairs * ceil_div(max_context_len, 256) < cus ? 128 : 256;
+  else
+    P = 512;
+  while (P < 512 && pairs * ceil_div(max_context_len, P) > 2 * cus) P *= 2;
+  while (ceil_div(max_context_len, P) > 64) P *= 2;
   return (int32_t)P;
 }
 

@@ -99,12 +99,16 @@ def test_workspace_size_formula():
     assert lib.pa_decode_workspace_bytes(-1, 2, 1, 64, 33, 16) == 0
 
 
-def test_partition_choice_is_a_multiple_of_16():
+def test_partition_choice():
+    # the rule (256 compute units assumed without a GPU): one pass up to 512 tokens or when
+    # the (sequence, KV head) pairs fill the device twice; 128 / 256 up to 4096 tokens; 512
+    # beyond, doubled while a sequence would need more than 64 partitions
     lib = pa.load()
-    for B, Hkv, L in [(1, 2, 2048), (64, 2, 2512), (16, 2, 8192), (4, 1, 33), (1000, 8, 100)]:
-        p = lib.pa_decode_partition_size(B, Hkv, L)
-        assert p == 0 or (p % 16 == 0 and 64 <= p <= 512 and p < L)
-    assert lib.pa_decode_partition_size(1000, 8, 4096) == 0  # enough (seq, head) pairs alone
+    for (B, Hkv, L), want in [((1, 2, 2048), 128), ((4, 2, 2048), 128), ((64, 2, 2512), 512), ((64, 2, 1024), 256),
+                              ((8, 2, 4096), 256), ((16, 2, 8192), 512), ((1, 2, 32768), 512),
+                              ((1, 2, 65536), 1024), ((4, 1, 33), 0), ((1, 2, 512), 0),
+                              ((1, 2, 513), 128), ((1000, 8, 4096), 0), ((0, 2, 100), 0)]:
+        assert lib.pa_decode_partition_size(B, Hkv, L) == want, (B, Hkv, L)
 
 
 @pytest.mark.parametrize("kw,code", [
