@@ -192,14 +192,21 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   //    key below L), so NaN in unused slots cannot meet a zero probability.
   // Steps past the half's range are loaded the same way and never computed.
   struct Stage { u32x4_t k[K_LOADS]; u32x4_t v0[V_LOADS], v1[V_LOADS]; };  // native vectors: no memcpy, no stack
-  auto load_tile = [&](int tt) -> Stage {
+  // A step's four table entries are read one step before its data, so the
+  // four scalar loads are in flight together and their latency is hidden.
+  struct Entries { int e[kStepBlocks]; };
+  static_assert(kStepBlocks == 4, "four table entries per step");
+  auto load_entries = [&](int tt) -> Entries {
+    const int lb0 = tt * kStepBlocks;
+    Entries en;
+#pragma unroll
+    for (int i = 0; i < kStepBlocks; ++i) en.e[i] = bt_row[min(lb0 + i, nblk_seq - 1)];
+    return en;
+  };
+  auto load_tile = [&](int tt, const Entries& en) -> Stage {
     Stage st;
     const int lb0 = tt * kStepBlocks;
-    static_assert(kStepBlocks == 4, "four table entries per step");
-    const int ent0 = bt_row[min(lb0, nblk_seq - 1)];
-    const int ent1 = bt_row[min(lb0 + 1, nblk_seq - 1)];
-    const int ent2 = bt_row[min(lb0 + 2, nblk_seq - 1)];
-    const int ent3 = bt_row[min(lb0 + 3, nblk_seq - 1)];
+    const int ent0 = en.e[0], ent1 = en.e[1], ent2 = en.e[2], ent3 = en.e[3];
 #pragma unroll
     for (int i = 0; i < K_LOADS; ++i) {
       // chunk c: block c / (16 NCH), key row, 16-byte chunk (coalesced rows)
@@ -294,6 +301,17 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         for (int ks = 0; ks < KS; ++ks) st[kt][rt] = mfma_bf16(ka[ks], qb[rt][ks], st[kt][rt]);
       }
     }
+    // V^T operands of the first key pair: their LDS reads are in flight during
+    // the softmax (the second pair's are issued at the start of the products)
+    auto read_vt = [&](int pp, int dt) {
+      return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                                              vt_base + (dt * 16 + col) * kVtStride + pp * 32 + quad * 8));
+    };
+    bf16x8_t va0[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) va0[dt] = read_vt(0, dt);
+    __builtin_amdgcn_sched_barrier(0);
+
     // causal limits: only steps crossing some row's diagonal need the selects
     if (key0 + kStepKeys - 1 > lim_min_wg) {
 #pragma unroll
@@ -309,12 +327,13 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     bf16x8_t pb[kPairs][kRowTiles];
 #pragma unroll
     for (int rt = 0; rt < kRowTiles; ++rt) {
-      float mt = -INFINITY;
+      // scores are finite or a masked -inf here, so the NaN-propagating max is exact
+      float mt = maxn(maxn(st[0][rt][0], st[0][rt][1]), maxn(st[0][rt][2], st[0][rt][3]));
 #pragma unroll
-      for (int kt = 0; kt < kStepBlocks; ++kt)
-        mt = fmaxf(mt, fmaxf(fmaxf(st[kt][rt][0], st[kt][rt][1]), fmaxf(st[kt][rt][2], st[kt][rt][3])));
-      mt = fmaxf(mt, swap16(mt));
-      mt = fmaxf(mt, swap32(mt));
+      for (int kt = 1; kt < kStepBlocks; ++kt)
+        mt = maxn(maxn(mt, st[kt][rt][0]), maxn(maxn(st[kt][rt][1], st[kt][rt][2]), st[kt][rt][3]));
+      mt = maxn_swap16(mt);
+      mt = maxn_swap32(mt);
       const bool raise = mt > m_ref[rt] + lazy_raw;  // false for -inf steps
       if (__builtin_amdgcn_ballot_w64(raise)) {
         // rows that keep their reference scale by exactly 1 (their m_ref may be -inf)
@@ -342,26 +361,29 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     }
 
     // ---- PV: O^T += V^T P^T per 32-key pair -------------------------------------------
+    static_assert(kPairs == 2, "two key pairs per step");
+    bf16x8_t va1[DT];
 #pragma unroll
-    for (int pp = 0; pp < kPairs; ++pp) {
-      bf16x8_t va[DT];
+    for (int dt = 0; dt < DT; ++dt) va1[dt] = read_vt(1, dt);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        va[dt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                                                  vt_base + (dt * 16 + col) * kVtStride + pp * 32 + quad * 8));
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int rt = 0; rt < kRowTiles; ++rt) o[dt][rt] = mfma_bf16(va0[dt], pb[0][rt], o[dt][rt]);
 #pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) o[dt][rt] = mfma_bf16(va[dt], pb[pp][rt], o[dt][rt]);
-    }
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt) o[dt][rt] = mfma_bf16(va1[dt], pb[1][rt], o[dt][rt]);
   };
 
   // ---- main loop: both halves in step; steps past a half's range are skipped ---------
-  store_tile(load_tile(tile0), 0);
+  store_tile(load_tile(tile0, load_entries(tile0)), 0);
+  Entries en_next = load_entries(tile0 + 1);
   __syncthreads();
   for (int i = 0; i < nsteps; ++i) {
     // the next step's loads are in flight while this one computes
-    const Stage nx = load_tile(tile0 + i + 1);
+    const Stage nx = load_tile(tile0 + i + 1, en_next);
+    en_next = load_entries(tile0 + i + 2);
     if (tile0 + i < tile_end) compute_tile(tile0 + i, i & 1);
     store_tile(nx, (i + 1) & 1);
     __syncthreads();

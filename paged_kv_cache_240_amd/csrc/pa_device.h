@@ -135,6 +135,19 @@ __device__ __forceinline__ float swap32(float x) {
   return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// IEEE maximum (a NaN operand gives NaN).  Unlike fmaxf it needs no
+// canonicalising of its operands, and chains of it fold into three-input
+// v_maximum3_f32.
+__device__ __forceinline__ float maxn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// maxn of x and the value the partner row holds (16-lane rows 0<->1 and
+// 2<->3, or the two 32-lane halves), in every lane.  The partner's value is
+// taken with the lane select of swap16 / swap32: a maximum of the two
+// results of a permlane swap of x with itself is folded by the compiler to
+// the first result alone, which drops the partner in half of the lanes.
+__device__ __forceinline__ float maxn_swap16(float x) { return maxn(x, swap16(x)); }
+__device__ __forceinline__ float maxn_swap32(float x) { return maxn(x, swap32(x)); }
+
 // Reductions over the 64 lanes of a wave, result in every lane.
 __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]

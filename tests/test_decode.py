@@ -72,6 +72,16 @@ def test_head_shapes_and_ragged_lengths(gpu, D, G):
         assert (out[0] == 0).all()
 
 
+def test_wide_score_range(gpu):
+    # q scaled by 64 (exact in bf16): scores spread over hundreds
+    b = W.decode_batch([1, 17, 300, 1025, 4096], 12, 2, 128, 512, 1090, theta=1e4)
+    b.q = (b.q.float() * 64).to(torch.bfloat16)
+    ref = oracle_decode(as_bits(b.q), as_bits(b.k_cache), as_bits(b.v_cache), b)
+    g = b.to("cuda")
+    for P in (0, 16, 64, 512, -1):
+        assert_attention_close(gpu_decode(gpu, g, P), ref, f"q x 64 P={P}")
+
+
 def test_block_permutation_and_rerun_bit_identical(gpu):
     b = W.cb_step()
     g = b.to("cuda")

@@ -58,6 +58,14 @@ def test_head_shapes(gpu, D, G, Hkv, nq):
     _run(gpu, b, nq, [0, 64, 512], f"G={G} Hkv={Hkv} nq={nq} D={D}")
 
 
+def test_wide_score_range(gpu):
+    # q scaled by 64 (exact in bf16): a row maximum taken too low would overflow
+    lens = [5, 40, 300, 1025, 2048]
+    b = W.verify_batch(lens, 5, 12, 2, 128, 512, 3450, theta=1e4)
+    b.q = (b.q.float() * 64).to(torch.bfloat16)
+    _run(gpu, b, 5, [0, 64, 512, -1], "q x 64")
+
+
 def test_one_query_is_decode(gpu):
     # NQ = 1 is a decode step: both entry points agree with the oracle and closely with each other
     b = W.verify_batch([1, 15, 16, 33, 700, 2048], 1, 12, 2, 128, 256, 3501)

@@ -66,6 +66,15 @@ def test_empty_chunks_and_long_prompt(gpu):
     assert b.T == 1003
 
 
+def test_wide_score_range(gpu):
+    # q scaled by 64 (exact in bf16): scores spread over hundreds, so a row
+    # maximum taken too low by more than about 2^7 in the exponent would
+    # overflow the bf16 probabilities and show as a non-finite output
+    b = W.prefill_batch([0, 40, 300, 1000], [130, 64, 200, 24], 12, 2, 128, 256, 3104, theta=1e4)
+    b.q = (b.q.float() * 64).to(torch.bfloat16)
+    _store_then_prefill(gpu, b, "q x 64")
+
+
 def test_rerun_bit_identical(gpu):
     b = W.prefill_batch([100, 3], [200, 77], 12, 2, 128, 64, 3103, theta=1e6)
     g = b.to("cuda")
