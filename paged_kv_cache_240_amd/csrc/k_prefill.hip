@@ -152,7 +152,6 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   const int ntiles = (kmax - kbeg + kStepKeys - 1) / kStepKeys;
   const int nsteps = (ntiles + 1) / 2;                 // tiles of half 0 (half 1 has <= as many)
   const int tile0 = tbase + half * nsteps;             // first tile of this wave's half
-  const int tile_end = tbase + (half == 0 ? nsteps : ntiles);  // one past its last tile
   const int nblk_seq = (L + kBlockSize - 1) / kBlockSize;
   const int32_t* bt_row = block_tables + (int64_t)seq_first * max_blocks;
   const int64_t head_off = (int64_t)g * kBlockSize * D;
@@ -276,14 +275,21 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
                                                                 0x3F803F80u, 0x3F803F80u));
 
-  // one step of this half from LDS buffer `buf`
-  auto compute_tile = [&](int tt, int buf) {
+  // One step of this half from LDS buffer `buf`, then the next step's tile
+  // into the other buffer.  DIAG: some key of the step is past some row's
+  // causal limit, so scores need the selects; the two instantiations keep each
+  // step one straight-line block, so the row maxima interleave with the QK
+  // products and the store of the next tile with the PV products.
+  auto step = [&](auto diag_c, int tt, int buf, const Stage& nx) {
+    constexpr bool DIAG = decltype(diag_c)::value;
     const unsigned char* ks_base = lds[half][buf];
     const uint16_t* vt_base = reinterpret_cast<const uint16_t*>(lds[half][buf] + KS_BYTES);
     const int key0 = tt * kStepKeys;
 
-    // ---- QK: S^T for kStepBlocks key tiles x 2 row tiles -------------------------
+    // ---- QK: S^T for kStepBlocks key tiles x 2 row tiles, row maxima as they come
+    // (scores are finite or a masked -inf, so the NaN-propagating max is exact)
     floatx4_t st[kStepBlocks][kRowTiles];
+    float mt[kRowTiles];
 #pragma unroll
     for (int kt = 0; kt < kStepBlocks; ++kt) {
       const int key = kt * 16 + col;
@@ -300,6 +306,16 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) st[kt][rt] = mfma_bf16(ka[ks], qb[rt][ks], st[kt][rt]);
       }
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt) {
+        if constexpr (DIAG) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            st[kt][rt][j] = key0 + kt * 16 + quad * 4 + j <= lim[rt] ? st[kt][rt][j] : -INFINITY;
+        }
+        const float m4 = maxn(maxn(st[kt][rt][0], st[kt][rt][1]), maxn(st[kt][rt][2], st[kt][rt][3]));
+        mt[rt] = kt == 0 ? m4 : maxn(mt[rt], m4);
+      }
     }
     // V^T operands of the first key pair: their LDS reads are in flight during
     // the softmax (the second pair's are issued at the start of the products)
@@ -312,82 +328,92 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     for (int dt = 0; dt < DT; ++dt) va0[dt] = read_vt(0, dt);
     __builtin_amdgcn_sched_barrier(0);
 
-    // causal limits: only steps crossing some row's diagonal need the selects
-    if (key0 + kStepKeys - 1 > lim_min_wg) {
-#pragma unroll
-      for (int kt = 0; kt < kStepBlocks; ++kt)
-#pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            st[kt][rt][j] = key0 + kt * 16 + quad * 4 + j <= lim[rt] ? st[kt][rt][j] : -INFINITY;
-    }
-
     // ---- P: softmax numerators against a lazily raised reference max ------------
-    bf16x8_t pb[kPairs][kRowTiles];
+    bool raise[kRowTiles];
+    bool any = false;
 #pragma unroll
     for (int rt = 0; rt < kRowTiles; ++rt) {
-      // scores are finite or a masked -inf here, so the NaN-propagating max is exact
-      float mt = maxn(maxn(st[0][rt][0], st[0][rt][1]), maxn(st[0][rt][2], st[0][rt][3]));
+      mt[rt] = maxn_swap32(maxn_swap16(mt[rt]));
+      raise[rt] = mt[rt] > m_ref[rt] + lazy_raw;  // false for -inf steps
+      any = any || raise[rt];
+    }
+    if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
-      for (int kt = 1; kt < kStepBlocks; ++kt)
-        mt = maxn(maxn(mt, st[kt][rt][0]), maxn(maxn(st[kt][rt][1], st[kt][rt][2]), st[kt][rt][3]));
-      mt = maxn_swap16(mt);
-      mt = maxn_swap32(mt);
-      const bool raise = mt > m_ref[rt] + lazy_raw;  // false for -inf steps
-      if (__builtin_amdgcn_ballot_w64(raise)) {
+      for (int rt = 0; rt < kRowTiles; ++rt) {
         // rows that keep their reference scale by exactly 1 (their m_ref may be -inf)
-        const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref[rt] - mt) * scale_log2) : 1.f;
-        m_ref[rt] = raise ? mt : m_ref[rt];
+        const float alpha = raise[rt] ? __builtin_amdgcn_exp2f((m_ref[rt] - mt[rt]) * scale_log2) : 1.f;
+        m_ref[rt] = raise[rt] ? mt[rt] : m_ref[rt];
         lacc[rt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
       }
-      const float refc = m_ref[rt] == -INFINITY ? 0.f : m_ref[rt] * scale_log2;
-#pragma unroll
-      for (int pp = 0; pp < kPairs; ++pp) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const floatx4_t& sv = st[2 * pp + h][rt];
-          pk[2 * h] = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[0], scale_log2, -refc)),
-                                 __builtin_amdgcn_exp2f(fmaf(sv[1], scale_log2, -refc)));
-          pk[2 * h + 1] = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[2], scale_log2, -refc)),
-                                     __builtin_amdgcn_exp2f(fmaf(sv[3], scale_log2, -refc)));
-        }
-        pb[pp][rt] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-        lacc[rt] = mfma_bf16(ones, pb[pp][rt], lacc[rt]);
-      }
     }
+    float refc[kRowTiles];
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) refc[rt] = m_ref[rt] == -INFINITY ? 0.f : m_ref[rt] * scale_log2;
+    auto probs = [&](int pp, int rt) {
+      uint32_t pk[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const floatx4_t& sv = st[2 * pp + h][rt];
+        pk[2 * h] = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[0], scale_log2, -refc[rt])),
+                               __builtin_amdgcn_exp2f(fmaf(sv[1], scale_log2, -refc[rt])));
+        pk[2 * h + 1] = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[2], scale_log2, -refc[rt])),
+                                   __builtin_amdgcn_exp2f(fmaf(sv[3], scale_log2, -refc[rt])));
+      }
+      return __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    };
 
-    // ---- PV: O^T += V^T P^T per 32-key pair -------------------------------------------
+    // ---- PV: O^T += V^T P^T per 32-key pair; the second pair's probabilities are
+    // computed under the first pair's products, the next tile stored under the second's
     static_assert(kPairs == 2, "two key pairs per step");
+    bf16x8_t pb0[kRowTiles], pb1[kRowTiles];
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+      pb0[rt] = probs(0, rt);
+      lacc[rt] = mfma_bf16(ones, pb0[rt], lacc[rt]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt) o[dt][rt] = mfma_bf16(va0[dt], pb0[rt], o[dt][rt]);
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+      pb1[rt] = probs(1, rt);
+      lacc[rt] = mfma_bf16(ones, pb1[rt], lacc[rt]);
+    }
     bf16x8_t va1[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) va1[dt] = read_vt(1, dt);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) o[dt][rt] = mfma_bf16(va0[dt], pb[0][rt], o[dt][rt]);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) o[dt][rt] = mfma_bf16(va1[dt], pb[1][rt], o[dt][rt]);
+      for (int rt = 0; rt < kRowTiles; ++rt) o[dt][rt] = mfma_bf16(va1[dt], pb1[rt], o[dt][rt]);
+    store_tile(nx, buf ^ 1);
   };
 
-  // ---- main loop: both halves in step; steps past a half's range are skipped ---------
+  // ---- main loop: both halves in step ------------------------------------------------
+  // Half 1 may have one step fewer than half 0; it computes that step anyway
+  // (it would only wait at the barrier): the step's keys are past every row's
+  // causal limit, so all its scores are masked and its probabilities are 0.
+  // Steps needing the selects are the last ones of the range (tiles from
+  // (lim_min_wg + 1) / 64 on), so they run in a second loop: one step body per
+  // loop keeps the register allocation of each tight.  Both halves still run
+  // nsteps iterations, each ending in the one workgroup barrier.
   store_tile(load_tile(tile0, load_entries(tile0)), 0);
   Entries en_next = load_entries(tile0 + 1);
   __syncthreads();
-  for (int i = 0; i < nsteps; ++i) {
+  auto iteration = [&](auto diag_c, int i) {
     // the next step's loads are in flight while this one computes
     const Stage nx = load_tile(tile0 + i + 1, en_next);
     en_next = load_entries(tile0 + i + 2);
-    if (tile0 + i < tile_end) compute_tile(tile0 + i, i & 1);
-    store_tile(nx, (i + 1) & 1);
+    step(diag_c, tile0 + i, i & 1, nx);
     __syncthreads();
-  }
+  };
+  const int n_plain = min(max((lim_min_wg + 1) / kStepKeys - tile0, 0), nsteps);
+  int i = 0;
+  for (; i < n_plain; ++i) iteration(std::false_type{}, i);
+  for (; i < nsteps; ++i) iteration(std::true_type{}, i);
 
   // ---- merge the halves through LDS, normalise and write ------------------------------
   // lane holds O^T[dims 4*quad+j of tile dt][row col]; l of row col in lacc[rt][0]
