@@ -487,13 +487,12 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
       } else {
         if constexpr (step == kWaveBlocks) {
           // ---- P: online softmax over this wave's 8 blocks -------------------------
+          // scores are finite or a masked -inf, so the NaN-propagating max is exact
           float mx = -INFINITY;
 #pragma unroll
           for (int j = 0; j < kWaveBlocks; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, st[j][e]);
-          mx = fmaxf(mx, swap16(mx));
-          mx = fmaxf(mx, swap32(mx));
+            mx = maxn(maxn(mx, maxn(st[j][0], st[j][1])), maxn(st[j][2], st[j][3]));
+          mx = maxn_swap32(maxn_swap16(mx));
           const float m_new = fmaxf(m_run, mx);
           // no key of this head in range yet: m stays -inf and every p is 0
           const float ref = m_new == -INFINITY ? 0.f : m_new * scale_log2;

@@ -233,10 +233,10 @@ decode_multi_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
           // ---- P: the pair's probabilities against a lazily raised reference ------------
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
-            float mx = fmaxf(fmaxf(fmaxf(st[0][ct][0], st[0][ct][1]), fmaxf(st[0][ct][2], st[0][ct][3])),
-                             fmaxf(fmaxf(st[1][ct][0], st[1][ct][1]), fmaxf(st[1][ct][2], st[1][ct][3])));
-            mx = fmaxf(mx, swap16(mx));
-            mx = fmaxf(mx, swap32(mx));
+            // scores are finite or a masked -inf, so the NaN-propagating max is exact
+            float mx = maxn(maxn(maxn(st[0][ct][0], st[0][ct][1]), maxn(st[0][ct][2], st[0][ct][3])),
+                            maxn(maxn(st[1][ct][0], st[1][ct][1]), maxn(st[1][ct][2], st[1][ct][3])));
+            mx = maxn_swap32(maxn_swap16(mx));
             const bool raise = mx > m_ref[ct] + lazy_raw;  // false for -inf pairs
             if (__builtin_amdgcn_ballot_w64(raise)) {
               const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref[ct] - mx) * scale_log2) : 1.f;
