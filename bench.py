@@ -26,6 +26,8 @@ committed files only):
     python bench.py --mode partition-kernel  # 3 x 28 launches of the unfused partition kernel
     python bench.py --mode prefill-kernel  # 20 launches of the prefill kernel only
     python bench.py --mode copy-calibration  # torch copy of 1 GiB (FETCH/WRITE_SIZE scale)
+    python bench.py --mode write-traffic --pmc F_STEP W_STEP F_COPY W_COPY
+        # profiles/decode_partitions_traffic.json from the four counter folders
 """
 
 import argparse
@@ -540,6 +542,66 @@ def load_traffic(kernel_file, kernel_name):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _pmc_per_dispatch(folder, counter, kernel):
+    """Mean and count of one counter per dispatch of the kernels whose name contains
+    `kernel`, from a rocprofv3 --pmc csv folder (rows summed per dispatch)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    per = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter or kernel not in row.get("Kernel_Name", ""):
+                    continue
+                key = (fn, row.get("Dispatch_Id"))
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{counter}: no dispatch of {kernel!r} in {folder}")
+    vals = list(per.values())
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(dirs, layers):
+    """profiles/decode_partitions_traffic.json from four counter passes: FETCH_SIZE and
+    WRITE_SIZE of `--mode decode-kernel`, then of `--mode copy-calibration` (a 1 GiB
+    device copy whose true bytes scale the counters)."""
+    fetch_step, write_step, fetch_copy, write_copy = dirs
+    fk, n = _pmc_per_dispatch(fetch_step, "FETCH_SIZE", STEP_KERNEL)
+    wk, _ = _pmc_per_dispatch(write_step, "WRITE_SIZE", STEP_KERNEL)
+    fc, _ = _pmc_per_dispatch(fetch_copy, "FETCH_SIZE", "__amd_rocclr_copyBuffer")
+    wc, _ = _pmc_per_dispatch(write_copy, "WRITE_SIZE", "__amd_rocclr_copyBuffer")
+    copy_bytes = 1 << 30
+    fscale = copy_bytes / (fc * 1024)
+    wscale = copy_bytes / (wc * 1024)
+    rd = int(round(fk * 1024 * fscale))
+    wr = int(round(wk * 1024 * wscale))
+    b = W.long_decode_layer(0, device=torch.device("cpu"))
+    rec = {
+        "kernel": STEP_KERNEL,
+        "source": "paged_kv_cache_240_amd/csrc/k_decode.hip",
+        "source_sha256_16": kernel_source_hash("k_decode.hip"),
+        "workload": "long-context decode step, one layer: B=16, L=8192, Hq=12, Hkv=2, D=128, partition 512 "
+                    "(grid 16x2x16); the new token's RoPE + store folded in",
+        "fetch_size_kib_per_launch": round(fk, 1),
+        "write_size_kib_per_launch": round(wk, 1),
+        "fetch_scale": round(fscale, 5),
+        "write_scale": round(wscale, 5),
+        "hbm_read_bytes_per_launch": rd,
+        "hbm_write_bytes_per_launch": wr,
+        "hbm_bytes_per_launch": rd + wr,
+        "algorithmic_bytes_per_launch": step_kernel_bytes(b),
+        "launches": n,
+    }
+    path = os.path.join(ROOT, "profiles", "decode_partitions_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=2)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 # ---------------------------------------------------------------------------
 
 def main():
@@ -553,8 +615,14 @@ def main():
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--mode", default="bench",
                     choices=["bench", "decode-kernel", "partition-kernel", "prefill-kernel",
-                             "copy-calibration"])
+                             "copy-calibration", "write-traffic"])
+    ap.add_argument("--pmc", nargs=4, metavar=("FETCH_STEP", "WRITE_STEP", "FETCH_COPY", "WRITE_COPY"),
+                    help="write-traffic: the four rocprofv3 --pmc output folders")
     args = ap.parse_args()
+
+    if args.mode == "write-traffic":
+        write_traffic(args.pmc, args.layers)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
