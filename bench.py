@@ -567,7 +567,7 @@ def _pmc_per_dispatch(folder, counter, kernel):
     return sum(vals) / len(vals), len(vals)
 
 
-def write_traffic(dirs, layers):
+def write_traffic(dirs, path=None):
     """profiles/decode_partitions_traffic.json from four counter passes: FETCH_SIZE and
     WRITE_SIZE of `--mode decode-kernel`, then of `--mode copy-calibration` (a 1 GiB
     device copy whose true bytes scale the counters)."""
@@ -598,7 +598,7 @@ def write_traffic(dirs, layers):
         "algorithmic_bytes_per_launch": step_kernel_bytes(b),
         "launches": n,
     }
-    path = os.path.join(ROOT, "profiles", "decode_partitions_traffic.json")
+    path = path or os.path.join(ROOT, "profiles", "decode_partitions_traffic.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=2)
         f.write("\n")
@@ -624,7 +624,7 @@ def main():
     args = ap.parse_args()
 
     if args.mode == "write-traffic":
-        write_traffic(args.pmc, args.layers)
+        write_traffic(args.pmc)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
