@@ -296,25 +296,45 @@ def time_each(fn, reps, scrub=None, warm=10):
             "p90_us": round(float(np.percentile(t, 90)), 2), "reps": reps}
 
 
-def run_ceilings(device):
-    """Measured device limits beside the published ones: a streaming read of a
-    2 GiB buffer (eight times the last-level cache; best of three grid sizes)
-    and bf16 matrix-core throughput (4 independent chains per wave)."""
+def run_ceilings(device, layer_bytes):
+    """Measured device limits beside the published ones:
+      * a grid-stride streaming read of a 2 GiB buffer (eight times the
+        last-level cache; best of four grid sizes);
+      * a one-pass gather of the same buffer in scrambled 4 KiB tiles (a paged
+        K/V read without its arithmetic) -- the read ceiling;
+      * that gather over one layer's bytes per launch, each launch on another
+        slice of the buffer (cold): the floor for one decode launch's reads;
+      * bf16 matrix-core throughput (4 independent chains per wave)."""
     res = {"nominal_hbm_GBps": HBM_PEAK_GBPS, "nominal_mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFLOPS}
     nbytes = 1 << 31
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=device)
     best = 0.0
-    for grid in (1024, 2048, 4096):
+    for grid in (1024, 2048, 4096, 8192):
         us = time_calls(pa.prepare_probe_stream_read(buf, grid), 10, warm=2)
         best = max(best, nbytes / us / 1e3)
-    del buf
     res["stream_read_GBps"] = round(best, 1)
+    us = time_calls(pa.prepare_probe_gather_read(buf), 10, warm=2)
+    res["gather_read_GBps"] = round(nbytes / us / 1e3, 1)
+    res["read_ceiling_GBps"] = max(res["stream_read_GBps"], res["gather_read_GBps"])
+    slices = [pa.prepare_probe_gather_read(buf[i * (layer_bytes // 4):(i + 1) * (layer_bytes // 4)])
+              for i in range(nbytes // layer_bytes)]
+    state = {"i": 0}
+
+    def one_layer():
+        slices[state["i"] % len(slices)]()
+        state["i"] += 1
+
+    us = time_calls(one_layer, 4 * len(slices), warm=len(slices))
+    res["gather_read_one_layer"] = {"bytes": layer_bytes, "us_per_launch": round(us, 2),
+                                    "GBps": round(layer_bytes / us / 1e3, 1)}
+    del slices, buf
     iters, best = 20000, 0.0
     for grid in (512, 1024):
         us = time_calls(pa.prepare_probe_mfma_bf16(iters, grid, device), 3, warm=1)
         best = max(best, grid * 4 * iters * 4 * 16384 / us / 1e6)
     res["mfma_bf16_TFLOPs"] = round(best, 1)
-    res["note"] = "pa_probe_stream_read / pa_probe_mfma_bf16 on this device"
+    res["note"] = ("pa_probe_stream_read, pa_probe_gather_read, pa_probe_mfma_bf16 on this device; "
+                   "read_ceiling = the faster of the two reads")
     return res
 
 
@@ -734,9 +754,12 @@ def main():
         line["context"]["spec_verify_16x8192"] = run_verify(layers, args.steps, args.warmup)
         line["context"]["block_copies"] = run_blocks(dev)
         line["context"]["layer_ops"] = run_layer_ops(dev)
-        line["device_ceilings"] = run_ceilings(dev)
-        line["roofline"]["frac_of_measured_read"] = round(
-            line["roofline"]["achieved"] / line["device_ceilings"]["stream_read_GBps"], 4)
+        kv_layer = W.kv_bytes_logical(layers[0].context_lens.cpu().numpy(), layers[0].Hkv, layers[0].D)
+        dc = line["device_ceilings"] = run_ceilings(dev, kv_layer)
+        line["roofline"]["frac_of_measured_read"] = round(line["roofline"]["achieved"] / dc["read_ceiling_GBps"], 4)
+        # the launch against a pure read of the same K/V bytes in one launch
+        line["roofline"]["frac_of_one_layer_read"] = round(
+            dc["gather_read_one_layer"]["us_per_launch"] / line["roofline"]["avg_launch_us"], 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layers, args.cpu_budget)
     else:

@@ -6,6 +6,11 @@
 // stream_read: a grid-stride walk over a buffer with 16-byte non-temporal
 // loads, eight in flight per thread, folded into a 32-bit sum per lane so the
 // loads cannot be removed; one sum per workgroup is written.
+// gather_read: the buffer as 4 KiB tiles visited in a scrambled order (tile t
+// at (t * 0x9E3779B1) mod ntiles, a bijection for a power-of-two count), each
+// wave loading its 8 tiles with all 32 of its 16-byte loads in flight, then
+// leaving: one pass, the access granularity and the scattered placement of a
+// paged K/V read.  Sums as stream_read.
 // mfma_bf16: every wave runs `iters` rounds of four independent
 // v_mfma_f32_16x16x32_bf16 chains on operands of bf16 ones, so each
 // accumulator element ends at exactly 32 * iters; lane 0 of each wave writes
@@ -49,6 +54,41 @@ stream_read_kernel(const uint4* __restrict__ buf, int64_t n16, uint32_t* __restr
   }
 }
 
+constexpr int kTileWords16 = 4096 / 16;  // 16-byte pieces of a 4 KiB tile
+constexpr int kGatherTiles = 8;           // tiles per wave
+
+__global__ void __launch_bounds__(kProbeThreads)
+gather_read_kernel(const uint4* __restrict__ buf, int64_t ntiles, uint32_t* __restrict__ sums) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t0 = ((int64_t)blockIdx.x * (kProbeThreads / 64) + (threadIdx.x >> 6)) * kGatherTiles;
+  uint32_t acc = 0;
+  uint4 t[kGatherTiles][4];
+#pragma unroll
+  for (int j = 0; j < kGatherTiles; ++j) {
+    // tiles past the end re-read the last one and are not counted
+    const int64_t lt = min(t0 + j, ntiles - 1);
+    const int64_t tile = (int64_t)((uint64_t)lt * 0x9E3779B1ull & (uint64_t)(ntiles - 1));
+    const uint4* src = buf + tile * kTileWords16 + lane;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[j][k] = load_stream16(src + k * 64);
+  }
+#pragma unroll
+  for (int j = 0; j < kGatherTiles; ++j)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      acc += t0 + j < ntiles ? t[j][k].x + t[j][k].y + t[j][k].z + t[j][k].w : 0u;
+  __shared__ uint32_t part[kProbeThreads / 64];
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t s = 0;
+#pragma unroll
+    for (int w = 0; w < kProbeThreads / 64; ++w) s += part[w];
+    sums[blockIdx.x] = s;
+  }
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
@@ -73,6 +113,19 @@ hipError_t launch_probe_stream_read(const void* buf, int64_t bytes, uint32_t* su
                                     hipStream_t stream) {
   hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kProbeThreads), 0, stream,
                      static_cast<const uint4*>(buf), bytes / 16, sums);
+  return hipGetLastError();
+}
+
+int64_t probe_gather_read_groups(int64_t bytes) {
+  const int64_t per_group = (int64_t)(kProbeThreads / 64) * kGatherTiles;
+  return (bytes / 4096 + per_group - 1) / per_group;
+}
+
+hipError_t launch_probe_gather_read(const void* buf, int64_t bytes, uint32_t* sums,
+                                    hipStream_t stream) {
+  const int64_t groups = probe_gather_read_groups(bytes);
+  hipLaunchKernelGGL(gather_read_kernel, dim3((unsigned)groups), dim3(kProbeThreads), 0, stream,
+                     static_cast<const uint4*>(buf), bytes / 4096, sums);
   return hipGetLastError();
 }
 

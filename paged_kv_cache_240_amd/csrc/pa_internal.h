@@ -66,6 +66,12 @@ hipError_t launch_prefill(void* out, const void* q, const void* k_cache, const v
 hipError_t launch_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sums, int grid,
                                     hipStream_t stream);
 hipError_t launch_probe_mfma_bf16(int iters, float* out, int grid, hipStream_t stream);
+// A one-pass gather of `bytes` (a power-of-two count of 4 KiB tiles) in
+// scrambled 4 KiB tiles, one 32-bit sum per workgroup to
+// sums[probe_gather_read_groups(bytes)].
+int64_t probe_gather_read_groups(int64_t bytes);
+hipError_t launch_probe_gather_read(const void* buf, int64_t bytes, uint32_t* sums,
+                                    hipStream_t stream);
 
 // Shared-prefix decode: the group prefixes' partials (prefill kernel, group
 // mode), the suffix partitions of each sequence from starts[b], and their
