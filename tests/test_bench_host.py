@@ -44,3 +44,13 @@ def test_traffic_record_scales_counters_by_the_copy(tmp_path):
     assert rec["kernel"] == bench.STEP_KERNEL
     assert rec["source_sha256_16"] == bench.kernel_source_hash("k_decode.hip")
 
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says why."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
