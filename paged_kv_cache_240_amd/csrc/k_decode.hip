@@ -9,14 +9,17 @@
 // cached tokens of sequence b, K_b/V_b the rows of KV head h / G.
 //
 // Workgroup = 4 independent waves; the tokens of a partition (split-K) or of
-// the whole sequence (single pass) are walked in chunks of 32 blocks, wave w
-// taking blocks w, w+4, ..., w+28 of each chunk.  Both products run on
+// the whole sequence (single pass) are walked in chunks of 4*WB blocks, wave w
+// taking blocks w, w+4, ..., w+4(WB-1) of each chunk (WB = 8 blocks per wave
+// for partitions of more than 256 tokens and for single passes; 4 and 2 for
+// partitions of up to 256 and 128 tokens, whose ring then holds every block
+// of the wave at once).  Both products run on
 // v_mfma_f32_16x16x32_bf16 with the G query heads padded to 16:
 //   QK   S^T = K Q^T per block: the key tile is the A operand as it lies in
 //        memory (lane = key, 16 contiguous bytes of its row per k-step), the
 //        query rows the B operand.  A lane ends up with 4 consecutive keys of
 //        one head; rows past the range become -inf by a select.
-//   P    after the 8 blocks of a chunk, the running max per head (in-lane max,
+//   P    after the WB blocks of a chunk, the running max per head (in-lane max,
 //        then two cross-row swaps: a head's 32 keys of a block pair live in
 //        4 lanes), p = 2^((s - m) * scale * log2 e), rounded to bf16 in place:
 //        the 8 p of a lane for two blocks are exactly its A operand of PV.
@@ -28,8 +31,9 @@
 // Rows past the range are redirected to row 0 of their block when V is
 // loaded, so NaN in unused slots never meets a zero probability.
 // K and V blocks stream through a ring of DEPTH register buffers in the
-// order K0..K7, V0..V7, K0' ... so loads run DEPTH blocks ahead of the
-// arithmetic across phase and chunk boundaries.  Loads past the last block of
+// order K0..K(WB-1), V0..V(WB-1), K0' ... so loads run DEPTH blocks ahead of
+// the arithmetic across phase and chunk boundaries; with at most 4 blocks per
+// wave the ring holds all 2*WB, so no V load waits for a K block to arrive.  Loads past the last block of
 // the range re-read the last valid block (an L2 hit) instead of branching.
 // The waves never synchronise until the end, where their (max, sum, output)
 // triples are combined through LDS.  The output is the normalised bf16 row
@@ -47,9 +51,15 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kWaveBlocks = 8;                           // blocks per wave per chunk
+constexpr int kWaveBlocks = 8;                           // blocks per wave per chunk (streaming)
 constexpr int kChunkBlocks = kWaves * kWaveBlocks;       // 32
 constexpr int kChunkTokens = kChunkBlocks * kBlockSize;  // 512
+
+// Blocks per wave for a split-K launch whose partitions hold at most
+// `partition_size` tokens and fit one chunk.
+constexpr int wave_blocks_for(int partition_size) {
+  return partition_size <= kWaves * 2 * kBlockSize ? 2 : partition_size <= kWaves * 4 * kBlockSize ? 4 : 8;
+}
 constexpr int kDepth = 4;     // blocks in flight per wave when chunks repeat (ring slots must cycle per chunk)
 constexpr int kDepthOne = PA_DECODE_DEPTH_ONE;  // ... when the range is a single chunk
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // two bf16 1.0
@@ -233,12 +243,13 @@ __device__ __forceinline__ void substitute_v_rows(uint32_t (&slot)[SLOT], const 
       slot[r * HALF + w] = 4 * quad + r >= r_new ? v[w] : slot[r * HALF + w];
 }
 
-// ONE: the range is a single chunk (split-K with partitions of at most 512
-// tokens), so the ring need not cycle and can be deeper; no refills past it.
+// ONE: the range is a single chunk (split-K with partitions of at most
+// 4*WB blocks), so the ring need not cycle and can be deeper; no refills past it.
+// WB: blocks per wave per chunk (8, or 4 / 2 for short partitions).
 // FUSED: the decode step's store folded in (see launch_decode_step): q and
 // the new k arrive unrotated, and the new token's K/V row is written to the
 // cache and used from registers.
-template <int D, int G, bool SPLIT, bool ONE, bool FUSED>
+template <int D, int G, bool SPLIT, bool ONE, bool FUSED, int WB = kWaveBlocks>
 __global__ void __launch_bounds__(256, 2)  // 2 waves per SIMD: 8 streaming waves per CU
 decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
               const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
@@ -247,13 +258,17 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
               float* __restrict__ o_part, float* __restrict__ lse, const StepArgs st,
               const int32_t* __restrict__ starts) {
   static_assert(G >= 1 && G <= 8, "query heads per KV head: 1..8");
+  static_assert(WB == 2 || WB == 4 || WB == 8, "blocks per wave: 2, 4 or 8");
+  static_assert(ONE || WB == kWaveBlocks, "a cycling ring takes 8 blocks per wave");
+  constexpr int CHUNK_BLOCKS = kWaves * WB;
+  constexpr int CHUNK_TOKENS = CHUNK_BLOCKS * kBlockSize;
   constexpr int KS = D / 32;    // QK k-steps over the head dimension
   constexpr int DPL = D / 16;   // PV: dims per lane = output tiles of 16 columns
   constexpr int HALF = DPL / 2; // dwords of one V row piece
   constexpr int SLOT = 4 * KS;  // dwords per lane of a K block (16 bytes per k-step)
   static_assert(SLOT == 4 * HALF, "K and V blocks must occupy the same ring slot");
-  constexpr int STEPS = 2 * kWaveBlocks;  // K0..K7 then V0..V7
-  constexpr int DEPTH = ONE ? kDepthOne : kDepth;
+  constexpr int STEPS = 2 * WB;  // K0..K(WB-1) then V0..V(WB-1)
+  constexpr int DEPTH = ONE ? (2 * WB < kDepthOne ? 2 * WB : kDepthOne) : kDepth;
   static_assert(DEPTH % 2 == 0 && (ONE || STEPS % DEPTH == 0), "ring slots must repeat per chunk");
 
   __shared__ __align__(16) float red[kWaves][G][D];  // per-wave outputs, dim n*DPL+s at s*16+n
@@ -278,7 +293,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
   // it is replaced by the range's first block once L arrives), so the first
   // K/V loads wait for one round trip instead of two.
   const int lb0 = SPLIT ? (start + p * part_tokens) / kBlockSize : 0;
-  const int lb_spec = lb0 + wave + kWaves * (threadIdx.x & 7);
+  const int lb_spec = lb0 + wave + kWaves * (threadIdx.x & (WB - 1));
   const int ent_spec = bt_row[min(lb_spec, max_blocks - 1)];
   const int ent_first = bt_row[min(lb0, max_blocks - 1)];  // lb0 may lie past a short suffix
   const int col = lane & 15, quad = lane >> 4;  // MFMA lane roles
@@ -315,7 +330,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
   const int lb_new = nb_new - lb0;  // in this range
   const bool own_wg = FUSED && (!SPLIT || p == (L - 1 - start) / part_tokens);
   const bool owner = own_wg && wave == lb_new % kWaves;
-  const int c_new = lb_new / kChunkBlocks, i_new = (lb_new % kChunkBlocks) / kWaves;
+  const int c_new = lb_new / CHUNK_BLOCKS, i_new = (lb_new % CHUNK_BLOCKS) / kWaves;
   float cs_c[KS / 2][8], cs_s[KS / 2][8];
   uint4 kraw[KS];
   uint32_t vraw[HALF];
@@ -360,7 +375,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
 
   const int64_t head_off = (int64_t)g * kBlockSize * D;
   const int64_t blk_stride = (int64_t)Hkv * kBlockSize * D;
-  const int nchunks = ONE ? 1 : (t_end - t_begin + kChunkTokens - 1) / kChunkTokens;
+  const int nchunks = ONE ? 1 : (t_end - t_begin + CHUNK_TOKENS - 1) / CHUNK_TOKENS;
   const int last_lb = (t_end - 1) / kBlockSize;  // last logical block of the range
   const int lane_k = col * D + quad * 8;         // element offsets inside a block tile
   const int lane_v = col * DPL;
@@ -371,15 +386,15 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
   // the last valid entry.  Fetched a chunk ahead and read with readlane, so a
   // ring refill never waits on the table.
   auto fetch_entries = [&](int c) -> int {
-    const int lb = (t_begin + c * kChunkTokens) / kBlockSize + wave + kWaves * (lane & 7);
+    const int lb = (t_begin + c * CHUNK_TOKENS) / kBlockSize + wave + kWaves * (lane & (WB - 1));
     return bt_row[min(lb, last_lb)];
   };
   // Ring step `step` (0..7 K blocks, 8..15 V blocks) of the chunk whose
   // entries are `ent`; `left` = rows of that block inside the range.
   auto load_step = [&](uint32_t (&slot)[SLOT], int ent, int step, int left) {
-    const int i = step & (kWaveBlocks - 1);
+    const int i = step & (WB - 1);
     const int64_t base = (int64_t)__builtin_amdgcn_readlane(ent, i) * blk_stride + head_off;
-    if (step < kWaveBlocks) {
+    if (step < WB) {
       const uint16_t* src = k_cache + base + lane_k;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -401,11 +416,11 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
       }
     }
   };
-  auto rows_left = [&](int nt, int step) { return nt - (wave + kWaves * (step & 7)) * kBlockSize; };
+  auto rows_left = [&](int nt, int step) { return nt - (wave + kWaves * (step & (WB - 1))) * kBlockSize; };
 
   int ent_cur = lb_spec <= last_lb ? ent_spec : ent_first;  // == fetch_entries(0)
   int ent_nxt = ONE ? 0 : fetch_entries(nchunks > 1 ? 1 : 0);
-  const int nt0 = min(kChunkTokens, t_end - t_begin);
+  const int nt0 = min(CHUNK_TOKENS, t_end - t_begin);
   uint32_t ring[DEPTH][SLOT];
 #pragma unroll
   for (int s = 0; s < DEPTH; ++s) load_step(ring[s], ent_cur, s, rows_left(nt0, s));
@@ -453,18 +468,18 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
   }
 
   for (int c = 0; c < nchunks; ++c) {
-    const int c0 = t_begin + c * kChunkTokens;
-    const int nt = min(kChunkTokens, t_end - c0);  // valid tokens of the chunk
-    const int nt_next = min(kChunkTokens, t_end - c0 - kChunkTokens);
-    floatx4_t st[kWaveBlocks];  // raw scores: keys 4*quad+e of block i, head col
-    uint4 pa[kWaveBlocks / 2];  // bf16 probabilities: A operand of block pair j
+    const int c0 = t_begin + c * CHUNK_TOKENS;
+    const int nt = min(CHUNK_TOKENS, t_end - c0);  // valid tokens of the chunk
+    const int nt_next = min(CHUNK_TOKENS, t_end - c0 - CHUNK_TOKENS);
+    floatx4_t st[WB];  // raw scores: keys 4*quad+e of block i, head col
+    uint4 pa[WB / 2];  // bf16 probabilities: A operand of block pair j
 
     static_for<STEPS>([&](auto step_c) {
       constexpr int step = decltype(step_c)::value;
       uint32_t(&cur)[SLOT] = ring[step % DEPTH];
-      constexpr int i = step & (kWaveBlocks - 1);
+      constexpr int i = step & (WB - 1);
 
-      if constexpr (step < kWaveBlocks) {
+      if constexpr (step < WB) {
         // ---- QK on block i: S^T (16 keys x 16 heads) ---------------------------
         const int left = rows_left(nt, step);
         if constexpr (FUSED) {
@@ -485,12 +500,12 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
         if constexpr (ns < STEPS) load_step(cur, ent_cur, ns, rows_left(nt, ns));
         else if constexpr (!ONE) load_step(cur, ent_nxt, ns - STEPS, rows_left(nt_next, ns - STEPS));
       } else {
-        if constexpr (step == kWaveBlocks) {
+        if constexpr (step == WB) {
           // ---- P: online softmax over this wave's 8 blocks -------------------------
           // scores are finite or a masked -inf, so the NaN-propagating max is exact
           float mx = -INFINITY;
 #pragma unroll
-          for (int j = 0; j < kWaveBlocks; ++j)
+          for (int j = 0; j < WB; ++j)
             mx = maxn(maxn(mx, maxn(st[j][0], st[j][1])), maxn(st[j][2], st[j][3]));
           mx = maxn_swap32(maxn_swap16(mx));
           const float m_new = fmaxf(m_run, mx);
@@ -499,7 +514,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
           const float alpha = fast_exp2(m_run * scale_log2 - ref);
           m_run = m_new;
 #pragma unroll
-          for (int j = 0; j < kWaveBlocks / 2; ++j) {
+          for (int j = 0; j < WB / 2; ++j) {
             const floatx4_t& sa = st[2 * j];
             const floatx4_t& sb = st[2 * j + 1];
             pa[j].x = cvt_bf16x2(fast_exp2(fmaf(sa[0], scale_log2, -ref)), fast_exp2(fmaf(sa[1], scale_log2, -ref)));
@@ -530,7 +545,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
             // blocks i-1, i of this chunk, at or past the new block; two
             // separate tests on fixed slots: a merged call on a selected slot
             // address would force the whole ring into memory
-            const int lb_i = c * kChunkBlocks + wave + kWaves * i;  // block i in the range
+            const int lb_i = c * CHUNK_BLOCKS + wave + kWaves * i;  // block i in the range
             if (own_wg && lb_i - kWaves >= lb_new)
               substitute_v_rows<SLOT, HALF>(va, new_v + wave * HALF * 64, lane, r_new);
             __builtin_amdgcn_sched_barrier(0);
@@ -664,11 +679,17 @@ hipError_t launch_dg(void* out, float* o_part, float* lse, const void* q, const 
   auto* oo = static_cast<uint16_t*>(out);
   if (partition_size > 0) {
     const int np = (max_context_len + partition_size - 1) / partition_size;
-    if (partition_size <= kChunkTokens)
-      hipLaunchKernelGGL((decode_kernel<D, G, true, true, FUSED>), dim3(np, Hkv, B), dim3(256), 0,
-                         stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks,
-                         scale_log2, partition_size, np, oo, o_part, lse, st, starts);
-    else
+#define PA_ONE(WBB)                                                                           \
+  hipLaunchKernelGGL((decode_kernel<D, G, true, true, FUSED, WBB>), dim3(np, Hkv, B), dim3(256), 0, \
+                     stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks, scale_log2,   \
+                     partition_size, np, oo, o_part, lse, st, starts)
+    if (partition_size <= kChunkTokens) {
+      switch (wave_blocks_for(partition_size)) {
+        case 2: PA_ONE(2); break;
+        case 4: PA_ONE(4); break;
+        default: PA_ONE(8); break;
+      }
+    } else
       hipLaunchKernelGGL((decode_kernel<D, G, true, false, FUSED>), dim3(np, Hkv, B), dim3(256), 0,
                          stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks,
                          scale_log2, partition_size, np, oo, o_part, lse, st, starts);
@@ -677,6 +698,7 @@ hipError_t launch_dg(void* out, float* o_part, float* lse, const void* q, const 
                        stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks, scale_log2,
                        0, 1, oo, o_part, lse, st, nullptr);
   }
+#undef PA_ONE
   return hipGetLastError();
 }
 
@@ -754,13 +776,18 @@ hipError_t launch_decode_suffix(float* o_part, float* lse, const void* q, const 
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kc = static_cast<const uint16_t*>(k_cache);
   const auto* vc = static_cast<const uint16_t*>(v_cache);
+#define PA_SUF1(DD, GG, WBB)                                                                        \
+  hipLaunchKernelGGL((decode_kernel<DD, GG, true, true, false, WBB>), dim3(np, Hkv, B), dim3(256), 0, \
+                     stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks, scale_log2,    \
+                     partition_size, num_slots, nullptr, o_part, lse, none, starts)
 #define PA_SUF(DD, GG)                                                                             \
   do {                                                                                             \
-    if (partition_size <= kChunkTokens)                                                            \
-      hipLaunchKernelGGL((decode_kernel<DD, GG, true, true, false>), dim3(np, Hkv, B), dim3(256), 0, \
-                         stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks,           \
-                         scale_log2, partition_size, num_slots, nullptr, o_part, lse, none, starts); \
-    else                                                                                           \
+    if (partition_size <= kChunkTokens) {                                                          \
+      const int wb = wave_blocks_for(partition_size);                                              \
+      if (wb == 2) PA_SUF1(DD, GG, 2);                                                             \
+      else if (wb == 4) PA_SUF1(DD, GG, 4);                                                        \
+      else PA_SUF1(DD, GG, 8);                                                                     \
+    } else                                                                                         \
       hipLaunchKernelGGL((decode_kernel<DD, GG, true, false, false>), dim3(np, Hkv, B), dim3(256), 0, \
                          stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks,           \
                          scale_log2, partition_size, num_slots, nullptr, o_part, lse, none, starts); \
@@ -780,6 +807,7 @@ hipError_t launch_decode_suffix(float* o_part, float* lse, const void* q, const 
   if (D == 128) { PA_SUF_G(128) } else { PA_SUF_G(64) }
 #undef PA_SUF_G
 #undef PA_SUF
+#undef PA_SUF1
   return hipGetLastError();
 }
 
