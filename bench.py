@@ -49,7 +49,7 @@ import workloads as W  # noqa: E402
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 LONG_P = W.LONG_PARTITION
-STEP_KERNEL = "decode_kernel<128, 6, true, true, true>"
+STEP_KERNEL = "decode_kernel<128, 6, true, true, true, 8>"
 
 
 def _sync():
@@ -343,6 +343,7 @@ def run_context(device):
     scrub = torch.zeros(1 << 28, dtype=torch.int32, device=device)  # 1 GiB
     # batch 1, 2048 tokens: store + decode, library-chosen partitions, warm
     b = W.qwen_decode(device=device)
+    q_raw = b.q.clone()  # the decode step takes q unrotated; the separate store rotates b.q in place
     P = pa.decode_partition_size(b.B, b.Hkv, b.max_context_len)
     dec = pa.prepare_decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale,
                             b.max_context_len, partition_size=P)
@@ -354,13 +355,19 @@ def run_context(device):
         dec()
 
     us = time_calls(dec, 1000)
+    dstep = pa.prepare_decode_step(q_raw, b.k, b.v, b.k_cache, b.v_cache, b.block_tables,
+                                   b.context_lens, b.cos_sin, b.scale, b.max_context_len)
     res["qwen_b1_l2048"] = {"decode_us_per_call": round(us, 2), "partition_size": P,
                             "store_plus_decode_us": round(time_calls(step2, 1000), 2),
+                            "decode_step_us_per_call": round(time_calls(dstep, 1000), 2),
                             "kv_GBps": round(W.kv_bytes_logical([2048], 2, 128) / us / 1e3, 1),
                             "per_call_warm": time_each(dec, 1000),
                             "per_call_cold": time_each(dec, 50, scrub),
-                            "note": "decode_us_per_call: 1000 back-to-back calls in one event window; "
-                                    "per_call_*: one event pair around each call (adds the event cost)"}
+                            "note": "decode_us_per_call: pa_decode, 1000 back-to-back calls in one event "
+                                    "window; store_plus_decode_us: pa_cache_store + pa_decode; "
+                                    "decode_step_us_per_call: pa_decode_step (RoPE + store folded in); "
+                                    "per_call_*: pa_decode with one event pair around each call "
+                                    "(adds the event cost)"}
     # continuous-batching step: 64 sequences, 32 share a 2000-token prefix
     b = W.cb_step(device=device)
     P = pa.decode_partition_size(b.B, b.Hkv, b.max_context_len)
