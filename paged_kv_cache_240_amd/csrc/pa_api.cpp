@@ -117,26 +117,24 @@ pa_status pa_cache_store(void* q, const void* k, const void* v, void* k_cache, v
 }
 
 int32_t pa_decode_partition_size(int32_t B, int32_t Hkv, int32_t max_context_len) {
-  // Measured on MI355X (Qwen head shape): a partition costs a fixed latency
-  // (table, K/V and partial round trips) and the reduce is a launch of its
-  // own, cheap up to 64 partitions per sequence; so
-  //  * a batch that fills the device twice over, or contexts up to 512
-  //    tokens: one pass, no reduce;
-  //  * up to 4096 tokens: 256-token partitions, 128 when the batch would not
-  //    give every CU a workgroup;
-  //  * longer: 512-token partitions;
-  //  * doubled up to 512 while the grid would not be resident at once (two
-  //    workgroups per CU), and beyond while a sequence needs more than 64.
+  // Measured on MI355X (Qwen head shape, 1 to 128 sequences of 512 to 32768
+  // tokens): partitions of up to 256 tokens put every K/V load of a wave in
+  // flight at once, a launch runs best with up to two workgroups per CU, and
+  // the reduce is a launch of its own, cheap up to 64 partitions per sequence.
+  // So:
+  //  * (sequence, KV head) pairs that already give every CU a workgroup, or
+  //    contexts that fit one 128-token partition: one pass, no reduce;
+  //  * otherwise the smallest of 128, 256 and 512 tokens that keeps the grid
+  //    within two workgroups per CU and a sequence within 64 partitions;
+  //  * failing that, 512, doubled while a sequence needs more than 64.
   if (B <= 0 || Hkv <= 0 || max_context_len <= 0) return 0;
   const int64_t cus = device_cu_count();
   const int64_t pairs = (int64_t)B * Hkv;
-  if (pairs >= 2 * cus || max_context_len <= 512) return 0;
-  int64_t P;
-  if (max_context_len <= 4096)
-    P = pairs * ceil_div(max_context_len, 256) < cus ? 128 : 256;
-  else
-    P = 512;
-  while (P < 512 && pairs * ceil_div(max_context_len, P) > 2 * cus) P *= 2;
+  if (pairs >= cus || max_context_len <= 128) return 0;
+  for (int64_t P = 128; P <= 512; P *= 2)
+    if (pairs * ceil_div(max_context_len, P) <= 2 * cus && ceil_div(max_context_len, P) <= 64)
+      return (int32_t)P;
+  int64_t P = 512;
   while (ceil_div(max_context_len, P) > 64) P *= 2;
   return (int32_t)P;
 }

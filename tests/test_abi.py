@@ -100,14 +100,17 @@ def test_workspace_size_formula():
 
 
 def test_partition_choice():
-    # the rule (256 compute units assumed without a GPU): one pass up to 512 tokens or when
-    # the (sequence, KV head) pairs fill the device twice; 128 / 256 up to 4096 tokens; 512
-    # beyond, doubled while a sequence would need more than 64 partitions
+    # the rule (256 compute units assumed without a GPU): one pass when the (sequence, KV
+    # head) pairs give every CU a workgroup or the context fits 128 tokens; else the smallest
+    # of 128 / 256 / 512 keeping the grid within 2 workgroups per CU and 64 partitions per
+    # sequence; else 512, doubled while a sequence would need more than 64 partitions
     lib = pa.load()
     for (B, Hkv, L), want in [((1, 2, 2048), 128), ((4, 2, 2048), 128), ((64, 2, 2512), 512), ((64, 2, 1024), 256),
-                              ((8, 2, 4096), 256), ((16, 2, 8192), 512), ((1, 2, 32768), 512),
-                              ((1, 2, 65536), 1024), ((4, 1, 33), 0), ((1, 2, 512), 0),
-                              ((1, 2, 513), 128), ((1000, 8, 4096), 0), ((0, 2, 100), 0)]:
+                              ((8, 2, 4096), 128), ((4, 2, 8192), 128), ((16, 2, 8192), 512),
+                              ((32, 2, 4096), 512), ((1, 2, 8192), 128), ((1, 2, 16384), 256),
+                              ((1, 2, 32768), 512), ((1, 2, 65536), 1024), ((4, 1, 33), 0), ((1, 2, 128), 0),
+                              ((1, 2, 129), 128), ((1, 2, 512), 128), ((128, 2, 2048), 0), ((127, 2, 2048), 512),
+                              ((1000, 8, 4096), 0), ((0, 2, 100), 0)]:
         assert lib.pa_decode_partition_size(B, Hkv, L) == want, (B, Hkv, L)
 
 
