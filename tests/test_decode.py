@@ -66,7 +66,8 @@ def test_head_shapes_and_ragged_lengths(gpu, D, G):
     b.context_lens = torch.tensor(lens, dtype=torch.int32)  # one empty sequence
     ref = oracle_decode(as_bits(b.q), as_bits(b.k_cache), as_bits(b.v_cache), b)
     g = b.to("cuda")
-    for P in (0, 16, 48, 512, -1):
+    # partitions of 2, 4 and 8 blocks per wave (up to 128, 256 and 512 tokens), and a single pass
+    for P in (0, 16, 48, 128, 208, 256, 512, -1):
         out = gpu_decode(gpu, g, P)
         assert_attention_close(out, ref, f"G={G} D={D} P={P}")
         assert (out[0] == 0).all()

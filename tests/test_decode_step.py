@@ -62,7 +62,7 @@ def test_ragged_lengths_and_partition_edges(gpu, D, G):
     Hkv = 2 if G <= 4 else 1
     b = W.decode_batch(lens, G * Hkv, Hkv, D, 512, 5100 + 10 * G + D, theta=1e4, poison=True,
                        table_fill=W.INT32_MIN)
-    _check(gpu, b, [0, 16, 48, 64, 512, 1024, -1], f"G={G} D={D}")
+    _check(gpu, b, [0, 16, 48, 64, 128, 144, 256, 512, 1024, -1], f"G={G} D={D}")
 
 
 def test_qwen_batch1(gpu):
