@@ -75,7 +75,8 @@ const char* pa_status_str(pa_status s);
  *   k_cache[s / bs][g][s % bs][:] = bf16(rope(k[i][g][:], p))  for every KV head g
  *   v_cache[s / bs][g][s % bs][:] = v[i][g][:]  (bits copied)  for every KV head g
  *   q[i][h][:]                    = bf16(rope(q[i][h][:], p))  for every query head h (in place)
- * A token with a negative slot is padding: nothing is read or written for it.
+ * A token with a negative slot is padding: nothing is written for it (its q,
+ * k and v rows may be read, and q is left unchanged).
  * rope pairs element j with element j + D/2 (j < D/2):
  *   y[j]       = fl(fl(x[j] * c[j]) - fl(x[j + D/2] * s[j]))
  *   y[j + D/2] = fl(fl(x[j + D/2] * c[j]) + fl(x[j] * s[j]))
@@ -108,11 +109,12 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
 
 /*
  * The partition size pa_decode uses when asked to choose (partition_size
- * -1): 0 (single pass) when B * Hkv alone fills the GPU twice over or the
- * contexts are at most 512 tokens; up to 4096 tokens, 256 (128 when the batch
- * would not give every compute unit a workgroup); longer, 512; doubled up to
- * 512 while the grid would exceed two workgroups per compute unit, and beyond
- * while a sequence would need more than 64 partitions.  Host-only; reads the
+ * -1): 0 (single pass) when the B * Hkv (sequence, KV head) pairs alone give
+ * every compute unit a workgroup, or when max_context_len is at most 128;
+ * otherwise the smallest of 128, 256 and 512 tokens whose grid,
+ * B * Hkv * ceil(max_context_len / P), stays within two workgroups per compute
+ * unit with at most 64 partitions per sequence; failing that 512, doubled while
+ * a sequence would need more than 64 partitions.  Host-only; reads the
  * device's compute-unit count once.
  */
 int32_t pa_decode_partition_size(int32_t B, int32_t Hkv, int32_t max_context_len);
@@ -128,7 +130,8 @@ int32_t pa_decode_partition_size(int32_t B, int32_t Hkv, int32_t max_context_len
  * to bf16 (nearest even).
  *
  * out, q          bf16 [B][Hq][D]; out may not alias q.
- * block_tables    int32 [B][max_blocks]; entries past ceil(L_b/16) are never read.
+ * block_tables    int32 [B][max_blocks]; entries past ceil(L_b/16) may be
+ *                 loaded (inside the row) but are never used as block ids.
  * context_lens    int32 [B].
  * max_context_len host-known bound on context_lens (sizes the grid; no
  *                 device-to-host read).
@@ -467,44 +470,6 @@ pa_status pa_bm_swap_out(pa_block_manager* m, int64_t seq_id, int32_t* device_bl
                          int32_t* host_blocks, int32_t capacity, int32_t* n);
 pa_status pa_bm_swap_in(pa_block_manager* m, int64_t seq_id, int32_t* host_blocks,
                         int32_t* device_blocks, int32_t capacity, int32_t* n);
-
-/*
- * Device ceilings, for the rooflines of the entry points above: the pages
- * call decode bandwidth-bound and prefill compute-bound ([T4 engine];
- * [Pico-vLLM] "H200 comparison"), and these two kernels measure the
- * corresponding limits of the device they run on.  Measurement only.
- *
- * pa_probe_stream_read: reads `bytes` (a positive multiple of 16) of device
- * memory at buf once, with 16-byte non-temporal loads from `grid` workgroups
- * of 256 threads, and writes the 32-bit wrap-around sum of the buffer's
- * 32-bit words seen by workgroup w to sums[w] (sums: uint32 [grid], device
- * memory); the grand total equals the sum of all words of the buffer mod 2^32.
- *
- * pa_probe_gather_read: reads `bytes` of device memory at buf once as 4 KiB
- * tiles (the size of one (block, KV head) tile of a paged pool at head_dim 128)
- * in a scrambled order, each wave of 64 lanes loading 8 tiles with all of its
- * loads in flight before it adds them: the access pattern of a paged K/V read
- * without its arithmetic.  bytes must be a positive multiple of 4096 whose
- * tile count is a power of two.  Workgroup w (of
- * pa_probe_gather_read_groups(bytes)) writes to sums[w] the 32-bit
- * wrap-around sum of the words it read; the grand total equals the sum of all
- * words of the buffer mod 2^32.  pa_probe_gather_read_groups returns 0 for
- * bytes <= 0.
- *
- * pa_probe_mfma_bf16: `grid` workgroups of 4 waves each run `iters` rounds of
- * four independent 16x16x32 bf16 matrix products per wave (16384 flop each);
- * wave v of workgroup w writes out[4*w + v] = 128 * iters exactly (out: fp32
- * [4*grid], device memory).  flop = grid * 4 * iters * 4 * 16384.
- *
- * PA_ERR_NULL for a NULL pointer, PA_ERR_SHAPE for non-positive sizes or a
- * byte count not a multiple of 16 (of 4096 with a power-of-two tile count for
- * the gather).
- */
-pa_status pa_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sums, int32_t grid,
-                               pa_stream_t stream);
-int64_t pa_probe_gather_read_groups(int64_t bytes);
-pa_status pa_probe_gather_read(const void* buf, int64_t bytes, uint32_t* sums, pa_stream_t stream);
-pa_status pa_probe_mfma_bf16(int32_t iters, float* out, int32_t grid, pa_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -52,10 +52,6 @@ _SIGS = {
     "pa_decode_shared_prefix": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
                                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p,
                                                _sz, _p]),
-    "pa_probe_stream_read": (ctypes.c_int, [_p, _i64, _p, _i32, _p]),
-    "pa_probe_mfma_bf16": (ctypes.c_int, [_i32, _p, _i32, _p]),
-    "pa_probe_gather_read_groups": (ctypes.c_int64, [_i64]),
-    "pa_probe_gather_read": (ctypes.c_int, [_p, _i64, _p, _p]),
     "pa_decode_step": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
     "pa_decode_step_partitions": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32,
@@ -129,9 +125,9 @@ class Call:
 
     __slots__ = ("name", "fn", "args", "result", "keep")
 
-    def __init__(self, name, args, result=None, keep=()):
+    def __init__(self, name, args, result=None, keep=(), lib=None):
         self.name = name
-        self.fn = getattr(load(), name)
+        self.fn = getattr(lib if lib is not None else load(), name)
         self.args = args
         self.result = result
         self.keep = keep  # the tensors whose pointers are in args stay alive with the call
@@ -738,42 +734,3 @@ class BlockManager:
     def swap_in(self, seq_id):
         """Returns (host_blocks, device_blocks): copy host -> device with pa_swap_blocks."""
         return self._swap("pa_bm_swap_in", seq_id)
-
-
-# ---------------------------------------------------------------------------
-# Device ceilings (measurement helpers)
-# ---------------------------------------------------------------------------
-
-def prepare_probe_stream_read(buf, grid=2048, sums=None):
-    """pa_probe_stream_read over a contiguous device tensor; returns a callable whose
-    result is the per-workgroup uint32 sums (as int32) of the buffer's 32-bit words."""
-    dev = buf.device
-    if not buf.is_contiguous() or buf.numel() * buf.element_size() % 16:
-        raise ValueError("buf must be contiguous and a multiple of 16 bytes")
-    if sums is None:
-        sums = torch.empty(grid, dtype=torch.int32, device=dev)
-    return Call("pa_probe_stream_read", (_ptr(buf), buf.numel() * buf.element_size(), _ptr(sums), grid,
-                                         _stream(dev)), result=sums, keep=(buf,))
-
-
-def prepare_probe_gather_read(buf, sums=None):
-    """pa_probe_gather_read over a contiguous device tensor (a power-of-two count of
-    4 KiB tiles); returns a callable whose result is the per-workgroup uint32 sums
-    (as int32) of the buffer's 32-bit words."""
-    dev = buf.device
-    nbytes = buf.numel() * buf.element_size()
-    tiles = nbytes // 4096
-    if not buf.is_contiguous() or nbytes % 4096 or tiles & (tiles - 1):
-        raise ValueError("buf must be contiguous and a power-of-two count of 4 KiB tiles")
-    groups = load().pa_probe_gather_read_groups(nbytes)
-    if sums is None:
-        sums = torch.empty(groups, dtype=torch.int32, device=dev)
-    return Call("pa_probe_gather_read", (_ptr(buf), nbytes, _ptr(sums), _stream(dev)),
-                result=sums, keep=(buf,))
-
-
-def prepare_probe_mfma_bf16(iters, grid, device, out=None):
-    """pa_probe_mfma_bf16; returns a callable whose result is out fp32 [4 * grid]."""
-    if out is None:
-        out = torch.empty(4 * grid, dtype=torch.float32, device=device)
-    return Call("pa_probe_mfma_bf16", (int(iters), _ptr(out), int(grid), _stream(out.device)), result=out)

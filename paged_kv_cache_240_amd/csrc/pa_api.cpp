@@ -461,29 +461,4 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
                                      scale, static_cast<hipStream_t>(stream)));
 }
 
-pa_status pa_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sums, int32_t grid,
-                               pa_stream_t stream) {
-  if (!buf || !sums) return PA_ERR_NULL;
-  if (bytes <= 0 || bytes % 16 != 0 || grid <= 0) return PA_ERR_SHAPE;
-  return from_hip(pa::launch_probe_stream_read(buf, bytes, sums, grid, static_cast<hipStream_t>(stream)));
-}
-
-int64_t pa_probe_gather_read_groups(int64_t bytes) {
-  return bytes > 0 ? pa::probe_gather_read_groups(bytes) : 0;
-}
-
-pa_status pa_probe_gather_read(const void* buf, int64_t bytes, uint32_t* sums, pa_stream_t stream) {
-  if (!buf || !sums) return PA_ERR_NULL;
-  const int64_t tiles = bytes / 4096;
-  if (bytes <= 0 || bytes % 4096 != 0 || (tiles & (tiles - 1)) != 0) return PA_ERR_SHAPE;
-  if (pa::probe_gather_read_groups(bytes) > 0x7fffffff) return PA_ERR_SHAPE;
-  return from_hip(pa::launch_probe_gather_read(buf, bytes, sums, static_cast<hipStream_t>(stream)));
-}
-
-pa_status pa_probe_mfma_bf16(int32_t iters, float* out, int32_t grid, pa_stream_t stream) {
-  if (!out) return PA_ERR_NULL;
-  if (iters <= 0 || grid <= 0) return PA_ERR_SHAPE;
-  return from_hip(pa::launch_probe_mfma_bf16(iters, out, grid, static_cast<hipStream_t>(stream)));
-}
-
 }  // extern "C"

@@ -1,0 +1,64 @@
+// Stand-ins for the kernel launchers of libpa, for the CPU-only sanitizer build
+// of the host code (pa_api.cpp, block_manager.cpp): every launch reports that no
+// device function is available, so an entry point that got past its host-side
+// validation returns PA_ERR_HIP instead of enqueueing anything.
+
+#include "../../paged_kv_cache_240_amd/csrc/pa_internal.h"
+
+namespace pa {
+namespace {
+hipError_t no_device() { return hipErrorInvalidDeviceFunction; }
+}  // namespace
+
+hipError_t launch_cache_store(void*, const void*, const void*, void*, void*, const int32_t*,
+                              const int32_t*, const float*, int, int, int, int, hipStream_t) {
+  return no_device();
+}
+hipError_t launch_decode(void*, float*, float*, const void*, const void*, const void*,
+                         const int32_t*, const int32_t*, int, int, int, int, int, int, float, int,
+                         hipStream_t) {
+  return no_device();
+}
+hipError_t launch_decode_step(void*, float*, float*, const void*, const void*, const void*, void*,
+                              void*, const int32_t*, const int32_t*, const float*, int, int, int,
+                              int, int, int, float, int, bool, hipStream_t) {
+  return no_device();
+}
+hipError_t launch_decode_multi(void*, float*, float*, const void*, const void*, const void*,
+                               const int32_t*, const int32_t*, int, int, int, int, int, int, int,
+                               float, int, hipStream_t) {
+  return no_device();
+}
+hipError_t launch_decode_combine(void*, const float*, const float*, const int32_t*, int, int, int,
+                                 int, int, hipStream_t) {
+  return no_device();
+}
+hipError_t launch_block_copy(void*, void*, const void*, const void*, const int32_t*,
+                             const int32_t*, int, int64_t, hipStream_t) {
+  return no_device();
+}
+hipError_t launch_rmsnorm(void*, void*, const void*, const void*, int, int, float, hipStream_t) {
+  return no_device();
+}
+hipError_t launch_swiglu(void*, const void*, int64_t, int, hipStream_t) { return no_device(); }
+hipError_t launch_prefill(void*, const void*, const void*, const void*, const int32_t*,
+                          const int32_t*, const int32_t*, int, int, int, int, int, int, float,
+                          hipStream_t) {
+  return no_device();
+}
+hipError_t launch_group_prefix(float*, float*, const void*, const void*, const void*,
+                               const int32_t*, const int32_t*, const int32_t*, int, int, int, int,
+                               int, int, int, int, int, int, float, hipStream_t) {
+  return no_device();
+}
+hipError_t launch_decode_suffix(float*, float*, const void*, const void*, const void*,
+                                const int32_t*, const int32_t*, const int32_t*, int, int, int, int,
+                                int, int, float, int, int, hipStream_t) {
+  return no_device();
+}
+hipError_t launch_decode_combine_cascade(void*, const float*, const float*, const int32_t*,
+                                         const int32_t*, int, int, int, int, int, int, int,
+                                         hipStream_t) {
+  return no_device();
+}
+}  // namespace pa

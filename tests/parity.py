@@ -1,13 +1,18 @@
 """Shared helpers of the GPU parity tests: run the library and the oracle on the
 same seeded inputs and compare.
 
-Attention tolerance (bf16 outputs y against the fp64 oracle x):
-  max criterion   max(|y - x| - ulp_bf16(x)/2) <= 1e-2
-  mean criterion  mean|y - bf16_rne(x)|          <= 1e-3
-Rounding x to bf16 alone can move it by half a bf16 ulp (0.0156 for |x| in
-[4, 8)), so the allowance of the max-abs bar is measured beyond that rounding,
-and the mean-abs bar against the correctly rounded oracle.  Raw max/mean abs
-errors are returned too.
+Attention tolerance (bf16 outputs y against the fp64 oracle x), the bar of
+1e-2 max-abs and 1e-3 mean-abs on bf16 outputs:
+  literal   max|y - x| <= 1e-2 and mean|y - x| <= 1e-3, asserted on every case
+            whose oracle output stays below 4 in magnitude (there half a bf16
+            ulp is at most 0.0078, so the max bar leaves room beyond rounding).
+            The mean bar is asserted where the correctly rounded oracle itself,
+            mean|bf16_rne(x) - x|, is at most 0.75e-3: for outputs spread like
+            N(0,1) that floor is about 1.1e-3, which no bf16 output can beat.
+  rounding  max(|y - x| - ulp_bf16(x)/2) <= 1e-2 and mean|y - bf16_rne(x)| <= 1e-3,
+            asserted on every case: the allowance measured beyond the rounding
+            of x to bf16 (half an ulp is 0.0156 for |x| in [4, 8)).
+Every error figure is returned, with the rounding floor and which bars applied.
 """
 
 import numpy as np
@@ -18,6 +23,8 @@ from workloads import as_bits, from_bits
 
 MAX_TOL = 1e-2
 MEAN_TOL = 1e-3
+LITERAL_BELOW = 4.0        # literal max/mean bars apply when max|x| < this
+LITERAL_MEAN_FLOOR = 0.75e-3  # ... and the mean bar when the rounding floor is at most this
 
 
 def attention_errors(y, x):
@@ -25,13 +32,23 @@ def attention_errors(y, x):
     yb = as_bits(y)
     yf = oracle.bf16_to_f64(yb)
     x = np.asarray(x, dtype=np.float64)
+    if x.size == 0:
+        return {"max_excess": 0.0, "mean_vs_rne": 0.0, "raw_max": 0.0, "raw_mean": 0.0,
+                "rne_floor_mean": 0.0, "max_abs_x": 0.0, "literal_max": True,
+                "literal_mean": True, "finite": True}
     excess = np.abs(yf - x) - oracle.bf16_ulp(x) / 2
     rne = oracle.bf16_to_f64(oracle.f64_to_bf16_rne(x))
+    max_abs_x = float(np.abs(x).max())
+    floor = float(np.abs(rne - x).mean())
     return {
-        "max_excess": float(excess.max()) if x.size else 0.0,
-        "mean_vs_rne": float(np.abs(yf - rne).mean()) if x.size else 0.0,
-        "raw_max": float(np.abs(yf - x).max()) if x.size else 0.0,
-        "raw_mean": float(np.abs(yf - x).mean()) if x.size else 0.0,
+        "max_excess": float(excess.max()),
+        "mean_vs_rne": float(np.abs(yf - rne).mean()),
+        "raw_max": float(np.abs(yf - x).max()),
+        "raw_mean": float(np.abs(yf - x).mean()),
+        "rne_floor_mean": floor,
+        "max_abs_x": max_abs_x,
+        "literal_max": max_abs_x < LITERAL_BELOW,
+        "literal_mean": max_abs_x < LITERAL_BELOW and floor <= LITERAL_MEAN_FLOOR,
         "finite": bool(np.isfinite(yf).all()),
     }
 
@@ -41,6 +58,10 @@ def assert_attention_close(y, x, label=""):
     assert e["finite"], f"{label}: non-finite output"
     assert e["max_excess"] <= MAX_TOL, f"{label}: {e}"
     assert e["mean_vs_rne"] <= MEAN_TOL, f"{label}: {e}"
+    if e["literal_max"]:
+        assert e["raw_max"] <= MAX_TOL, f"{label}: literal max-abs bar: {e}"
+    if e["literal_mean"]:
+        assert e["raw_mean"] <= MEAN_TOL, f"{label}: literal mean-abs bar: {e}"
     return e
 
 

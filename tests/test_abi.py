@@ -9,16 +9,18 @@ import re
 import pytest
 
 import paged_kv_cache_240_amd as pa
+from paged_kv_cache_240_amd import probes
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "pa_probe.h")
 
 OK, NULL, SHAPE, UNSUP, WS, HIP, MEM = range(7)
 P = ctypes.c_void_p(0x1000)  # a non-null dummy pointer: never dereferenced on these paths
 
 
-def declared_symbols():
-    text = open(HEADER).read()
+def declared_symbols(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
 
@@ -247,8 +249,21 @@ def test_decode_step_validation(kw, code):
     assert _step(**kw) == code
 
 
-def test_probe_validation():
+def test_probe_library_is_separate():
+    """The measurement kernels live in libpa_probe.so (include/pa_probe.h), not in the
+    paged-attention library: pa.h declares none of them and libpa.so exports none."""
+    assert not [s for s in declared_symbols() if s.startswith("pa_probe")]
     lib = pa.load()
+    for s in declared_symbols(PROBE_HEADER):
+        assert not hasattr(lib, s), s
+    plib = probes.load()
+    for s in declared_symbols(PROBE_HEADER):
+        assert hasattr(plib, s), s
+    assert os.path.samefile(probes.library_path, os.path.join(ROOT, "paged_kv_cache_240_amd", "libpa_probe.so"))
+
+
+def test_probe_validation():
+    lib = probes.load()
     assert lib.pa_probe_stream_read(None, 16, P, 1, None) == NULL
     assert lib.pa_probe_stream_read(P, 16, None, 1, None) == NULL
     assert lib.pa_probe_stream_read(P, 0, P, 1, None) == SHAPE

@@ -7,6 +7,8 @@ import numpy as np
 import pytest
 import torch
 
+from paged_kv_cache_240_amd import probes
+
 pytestmark = pytest.mark.gpu
 
 
@@ -15,7 +17,7 @@ def test_stream_read_sees_every_word_once(gpu, nbytes, grid):
     g = torch.Generator().manual_seed(nbytes)
     words = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32)
     want = int(words.numpy().view(np.uint32).astype(np.uint64).sum() % (1 << 32))
-    sums = gpu.prepare_probe_stream_read(words.cuda(), grid=grid)()
+    sums = probes.prepare_probe_stream_read(words.cuda(), grid=grid)()
     torch.cuda.synchronize()
     got = int(sums.cpu().numpy().view(np.uint32).astype(np.uint64).sum() % (1 << 32))
     assert got == want
@@ -28,7 +30,7 @@ def test_gather_read_sees_every_word_once(gpu, nbytes):
     g = torch.Generator().manual_seed(nbytes + 1)
     words = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32)
     want = int(words.numpy().view(np.uint32).astype(np.uint64).sum() % (1 << 32))
-    call = gpu.prepare_probe_gather_read(words.cuda())
+    call = probes.prepare_probe_gather_read(words.cuda())
     sums = call()
     torch.cuda.synchronize()
     assert sums.numel() == max(1, nbytes // 4096 // 32)
@@ -38,6 +40,6 @@ def test_gather_read_sees_every_word_once(gpu, nbytes):
 
 @pytest.mark.parametrize("iters,grid", [(1, 1), (7, 3), (1000, 512)])
 def test_mfma_probe_exact(gpu, iters, grid):
-    out = gpu.prepare_probe_mfma_bf16(iters, grid, "cuda")()
+    out = probes.prepare_probe_mfma_bf16(iters, grid, "cuda")()
     torch.cuda.synchronize()
     assert torch.equal(out.cpu(), torch.full((4 * grid,), 128.0 * iters))
