@@ -1,36 +1,38 @@
-// Causal paged chunked prefill for gfx950 on bf16 matrix cores.
+// Shared-prefix pass of the decode step for gfx950 on bf16 matrix cores: the
+// queries of a group of decode sequences that share their first blocks attend
+// that prefix once, together, and leave split-K partials for the reduce.
 //
-// Operation (Pico-vLLM write-up, §2: paged prefill kernel in the manner of
-// Flash Attention, using the matrix cores; mini-llm-engine post, §3.3: a
-// prompt is prefilled in chunks, each chunk attending the cached prefix plus
-// itself; §3.1: K/V in 16-token physical blocks behind a block table):
-// chunk row i of sequence b sits at position L_b - C_b + i and attends keys
-// t <= L_b - C_b + i with softmax(scale * q K^T) V, GQA head h -> KV head h/G.
+// Operation (mini-llm-engine post, §3.4: full blocks of a common prefix shared
+// by several sequences, ref_count > 1; Pico-vLLM write-up, §2: decode kernel in
+// the manner of Flash Attention, and the H200 comparison: Flash Decode's split
+// and log-sum-exp reduce): for every (sequence s of the group, query head h)
+// row and one partition [kbeg, kend) of the shared prefix, the partial
+// softmax(scale * q K^T) V over those keys, normalised, with its base-2
+// log-sum-exp; GQA query head h reads KV head h / G.
 //
-// Rows are (position, head) pairs of one (sequence, KV head), position-major
-// (r = pos * G + h), so the G query heads sharing a KV head share every K/V
-// tile.  Workgroup = 8 waves over 128 rows: the keys the rows can see are
-// split in two halves, and wave w takes row tiles 2(w%4), 2(w%4)+1 (16 rows
-// each) over half w/4.  Each half streams its keys in tiles of 32 (two
-// 16-token blocks) through a double-buffered LDS stage, filled from registers
-// loaded two tiles ahead.  Per tile and wave:
+// Rows are (sequence, head) pairs of one KV head, r = s * G + h, so the G
+// query heads sharing a KV head share every K/V tile.  Workgroup = 8 waves
+// over 128 rows: the partition's keys are split in two halves, and wave w takes
+// row tiles 2(w%4), 2(w%4)+1 (16 rows each) over half w/4.  Each half streams
+// its keys in steps of 64 (four 16-token blocks) through a double-buffered LDS
+// stage, filled from registers loaded one step ahead.  Per step and wave:
 //   QK   S^T (keys x rows) = K Q^T with v_mfma_f32_16x16x32_bf16: A = K tile
-//        from LDS (16-byte chunks XOR-swizzled by key so the 16 rows of an
-//        operand read hit distinct banks), B = the rows' queries (registers).
-//   P    per row (a lane column: 8 scores per lane, 4 lanes per row) the
-//        running reference max is raised only when a tile's max exceeds it by
-//        more than 2^8 (p then stays below 256: exact enough in bf16, safe in
-//        fp32 sums), which spares nearly every rescale of the accumulators.
-//        Causal limits are applied by selects on tiles crossing the diagonal.
+//        from LDS (16-byte chunks XOR-swizzled by key), B = the rows' queries
+//        (registers).
+//   P    per row the running reference max is raised only when a step's max
+//        exceeds it by more than 2^8 (p then stays below 256: exact enough in
+//        bf16, safe in fp32 sums), which spares nearly every rescale of the
+//        accumulators.  Keys past the partition end are masked by selects.
 //        p is rounded to bf16; the S^T accumulator layout is already the B
 //        operand of the PV product, so p never moves.
 //   PV   O^T (dims x rows) += V^T P^T: A = V^T from LDS, V stored transposed
 //        with the key order the P operand implies (8 keys of a lane
-//        contiguous) and an 80-byte row stride (conflict-free reads); a
+//        contiguous) and a 144-byte row stride (64 keys + 8 of padding); a
 //        ninth product against a ones operand accumulates the normaliser.
 // The two halves meet through LDS at the end (log-sum-exp merge).  Keys at or
-// past L are written to LDS as zeros (never multiplied by 0: NaN in unused
-// slots cannot leak) and their table entries are never read.
+// past the partition end are loaded from valid rows and never reach a product
+// with a nonzero weight; their table entries are never used as block ids.
+// (The chunked prefill itself is k_prefill_chunk.hip.)
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -90,7 +92,7 @@ struct GroupArgs {
   float* lse;       // [B][Hq][num_slots]
 };
 
-template <int D, int G, bool PART>
+template <int D, int G, bool PART>  // PART: the shared-prefix pass (the only mode launched)
 __global__ void __launch_bounds__(kThreads)
 prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
@@ -497,26 +499,6 @@ hipError_t launch_d(int G, dim3 grid, hipStream_t stream, uint16_t* out, const u
 }
 
 }  // namespace
-
-hipError_t launch_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
-                          const int32_t* block_tables, const int32_t* context_lens,
-                          const int32_t* query_start_loc, int B, int Hq, int Hkv, int D,
-                          int max_blocks, int max_query_len, float scale, hipStream_t stream) {
-  const int G = Hq / Hkv;
-  const int rblocks = (max_query_len * G + kRowsPerWG - 1) / kRowsPerWG;
-  const dim3 grid(rblocks, Hkv, B);
-  const float sl = scale * 1.4426950408889634f;
-  auto* o = static_cast<uint16_t*>(out);
-  auto* qq = static_cast<const uint16_t*>(q);
-  auto* kc = static_cast<const uint16_t*>(k_cache);
-  auto* vc = static_cast<const uint16_t*>(v_cache);
-  const GroupArgs none{};
-  if (D == 128)
-    return launch_d<128, false>(G, grid, stream, o, qq, kc, vc, block_tables, context_lens,
-                                query_start_loc, Hkv, max_blocks, sl, none);
-  return launch_d<64, false>(G, grid, stream, o, qq, kc, vc, block_tables, context_lens,
-                             query_start_loc, Hkv, max_blocks, sl, none);
-}
 
 // Shared-prefix partials of decode queries: grid (row blocks, Hkv, groups * parts).
 hipError_t launch_group_prefix(float* o_part, float* lse, const void* q, const void* k_cache,

@@ -456,6 +456,7 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
   if (B < 0 || T < 0 || max_blocks <= 0 || max_query_len < 0) return PA_ERR_SHAPE;
   if (B == 0 || T == 0 || max_query_len == 0) return PA_OK;
   if (max_query_len > T) return PA_ERR_SHAPE;
+  if (pa::prefill_workgroups(B, Hq, Hkv, max_query_len) > INT32_MAX) return PA_ERR_UNSUPPORTED;
   return from_hip(pa::launch_prefill(out, q, k_cache, v_cache, block_tables, context_lens,
                                      query_start_loc, B, Hq, Hkv, D, max_blocks, max_query_len,
                                      scale, static_cast<hipStream_t>(stream)));

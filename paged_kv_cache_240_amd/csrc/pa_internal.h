@@ -55,6 +55,8 @@ hipError_t launch_rmsnorm(void* out, void* residual, const void* x, const void* 
 
 hipError_t launch_swiglu(void* out, const void* gate_up, int64_t T, int I, hipStream_t stream);
 
+// Workgroups of the chunked-prefill launch (its grid is one-dimensional).
+int64_t prefill_workgroups(int B, int Hq, int Hkv, int max_query_len);
 hipError_t launch_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, const int32_t* context_lens,
                           const int32_t* query_start_loc, int B, int Hq, int Hkv, int D,

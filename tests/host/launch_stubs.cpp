@@ -41,6 +41,9 @@ hipError_t launch_rmsnorm(void*, void*, const void*, const void*, int, int, floa
   return no_device();
 }
 hipError_t launch_swiglu(void*, const void*, int64_t, int, hipStream_t) { return no_device(); }
+int64_t prefill_workgroups(int B, int Hq, int Hkv, int max_query_len) {
+  return ((int64_t)max_query_len * (Hq / Hkv) + 95) / 96 * Hkv * B;
+}
 hipError_t launch_prefill(void*, const void*, const void*, const void*, const int32_t*,
                           const int32_t*, const int32_t*, int, int, int, int, int, int, float,
                           hipStream_t) {
