@@ -48,6 +48,7 @@
 #include "pa_internal.h"
 
 
+
 namespace pa {
 namespace {
 
@@ -263,27 +264,25 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
           for (int j = 0; j < 4; ++j) st[t][rt][j] = j <= d ? st[t][rt][j] : -INFINITY;
         }
     }
+    // ---- P ----------------------------------------------------------------------
+    // The lane's own maximum per row decides whether any reference must move;
+    // only then is the row's maximum over its 4 lanes taken (almost never after
+    // the first step: later keys seldom exceed the reference by 2^8).
     float mt[kRowTiles];
+    bool any = false;
 #pragma unroll
     for (int rt = 0; rt < kRowTiles; ++rt) {
       mt[rt] = maxn(maxn(maxn(st[0][rt][0], st[0][rt][1]), maxn(st[0][rt][2], st[0][rt][3])),
                     maxn(maxn(st[1][rt][0], st[1][rt][1]), maxn(st[1][rt][2], st[1][rt][3])));
-    }
-
-    // ---- P ----------------------------------------------------------------------
-    bool raise[kRowTiles];
-    bool any = false;
-#pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
-      mt[rt] = maxn_swap32(maxn_swap16(mt[rt]));
-      raise[rt] = mt[rt] > m_ref[rt] + lazy_raw;  // false for all-masked steps
-      any = any || raise[rt];
+      any = any || mt[rt] > m_ref[rt] + lazy_raw;  // false for all-masked steps
     }
     if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
       for (int rt = 0; rt < kRowTiles; ++rt) {
-        const float alpha = raise[rt] ? __builtin_amdgcn_exp2f((m_ref[rt] - mt[rt]) * scale_log2) : 1.f;
-        m_ref[rt] = raise[rt] ? mt[rt] : m_ref[rt];
+        mt[rt] = maxn_swap32(maxn_swap16(mt[rt]));  // the row's maximum, the same in its 4 lanes
+        const bool raise = mt[rt] > m_ref[rt] + lazy_raw;
+        const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref[rt] - mt[rt]) * scale_log2) : 1.f;
+        m_ref[rt] = raise ? mt[rt] : m_ref[rt];
         lsum[rt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
