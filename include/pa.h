@@ -397,6 +397,30 @@ pa_status pa_rmsnorm_residual(void* out, void* residual, const void* x, const vo
 pa_status pa_swiglu(void* out, const void* gate_up, int64_t T, int32_t I, pa_stream_t stream);
 
 /*
+ * For callers that cannot allocate -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc: pa_decode with its split-K
+ * workspace in a file-scope device array of the library (one per GPU, held
+ * until the process ends) instead of a caller buffer.  Same arguments,
+ * semantics, results (bit for bit) and errors as pa_decode, minus workspace.
+ * Allocates nothing, on the host or the device.
+ *
+ * Limit: the workspace pa_decode would need, pa_decode_workspace_bytes(B, Hq,
+ * Hkv, D, max_context_len, P) for the partition size used, must be at most
+ * PA_DECODE_NOALLOC_SCRATCH_BYTES (16 MiB: e.g. 64 sequences x 12 query heads
+ * with 20 partitions at D = 128), else PA_ERR_WORKSPACE and nothing is
+ * enqueued.  All calls on one GPU share its array: calls that overlap on one
+ * GPU (other streams or threads) race and must not be issued.  The array's
+ * device address is looked up on the first call on each GPU; PA_ERR_HIP if
+ * that fails.
+ */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                            int32_t max_blocks, int32_t max_context_len, float scale,
+                            int32_t partition_size, pa_stream_t stream);
+
+/*
  * Host block manager ([mini-llm] §3.1 physical blocks with ref counts, O(1)
  * free list, per-sequence logical->physical table; §3.4 full blocks shared by
  * content hash, copy-on-write; §3.5 swap-out / swap-in; [Pico-vLLM] §3 LRU

@@ -58,6 +58,8 @@ _SIGS = {
                                                  _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p]),
     "pa_decode": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _f32, _i32, _p, _sz, _p]),
+    "pa_decode_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         _i32, _f32, _i32, _p]),
     "pa_decode_partitions": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, _f32, _i32, _p]),
     "pa_decode_combine": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p]),

@@ -311,3 +311,13 @@ def test_shared_prefix_workspace_size():
         64 * 12 * (2 + 16) * 129 * 4
     assert lib.pa_decode_shared_prefix_workspace_bytes(4, 12, 2, 128, 128, 0, 64) == 4 * 12 * 2 * 129 * 4
     assert lib.pa_decode_shared_prefix_workspace_bytes(4, 12, 2, 128, 128, 0, 24) == 0
+
+
+def test_noalloc_refuses_more_than_its_array():
+    """pa_decode_noalloc checks the workspace it would need against its 16 MiB
+    array before touching the device (no GPU is used here)."""
+    lib = pa.load()
+    assert lib.pa_decode_workspace_bytes(256, 12, 2, 128, 32768, 512) > 16 << 20
+    assert lib.pa_decode_noalloc(P, P, P, P, P, P, 256, 12, 2, 128, 16, 2048, 32768, 0.088, 512,
+                                 None) == WS
+    assert lib.pa_decode_noalloc(P, P, P, P, P, P, 2, 12, 2, 128, 16, 8, 128, 0.088, 24, None) == SHAPE
