@@ -257,6 +257,25 @@ pa_status pa_decode_step_partitions(float* o_part, float* lse, const void* q, co
                                          static_cast<hipStream_t>(stream)));
 }
 
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                            int32_t max_blocks, int32_t max_context_len, float scale,
+                            int32_t partition_size, pa_stream_t stream) {
+  // the workspace this call needs (0 for a single pass), checked before anything
+  // touches the device: more than the library's array is refused
+  if (partition_size < -1 || (partition_size > 0 && partition_size % 16 != 0)) return PA_ERR_SHAPE;
+  const int32_t P = resolve_partition(partition_size, B, Hkv, max_context_len);
+  const size_t need = P > 0 && B > 0 && max_context_len > 0
+                          ? pa_decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, P)
+                          : 0;
+  if (need > PA_DECODE_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  void* ws = pa::decode_scratch();
+  if (ws == nullptr) return PA_ERR_HIP;
+  return pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, D, block_size,
+                   max_blocks, max_context_len, scale, P, ws, PA_DECODE_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 namespace {
 constexpr int kPrefixPartTokens = 128;  // smallest shared-prefix partition: a key tile per half
 constexpr int kMaxCascadeSlots = 64;

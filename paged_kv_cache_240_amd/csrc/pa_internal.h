@@ -55,6 +55,11 @@ hipError_t launch_rmsnorm(void* out, void* residual, const void* x, const void* 
 
 hipError_t launch_swiglu(void* out, const void* gate_up, int64_t T, int I, hipStream_t stream);
 
+// The current device's address of the library's own split-K workspace of
+// PA_DECODE_NOALLOC_SCRATCH_BYTES (pa_decode_noalloc), looked up on its first
+// use on that device; NULL if the lookup fails.
+void* decode_scratch();
+
 // Workgroups of the chunked-prefill launch (its grid is one-dimensional).
 int64_t prefill_workgroups(int B, int Hq, int Hkv, int max_query_len);
 hipError_t launch_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -1,7 +1,7 @@
-// pa_decode_noalloc: pa_decode for callers that cannot allocate (code under
-// HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
-// The split-K partials live in a file-scope device array, `scratch`, instead
-// of a caller-provided workspace; everything else is pa_decode's path.
+// The device array behind pa_decode_noalloc (pa_api.cpp): pa_decode for callers
+// that cannot allocate (code under HIP graph capture, tight serving loops,
+// harnesses that forbid hipMalloc).  Its split-K partials live in a file-scope
+// device array, `scratch`, instead of a caller-provided workspace.
 //
 // The array's name in host code is a host-side stand-in, not a device
 // address, so it is never passed to a kernel: its device address on each GPU
@@ -16,6 +16,7 @@
 #include <mutex>
 
 #include "../../include/pa.h"
+#include "pa_internal.h"
 
 namespace {
 
@@ -48,24 +49,6 @@ void* device_scratch() {
 
 }  // namespace
 
-extern "C" pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache,
-                                       const void* v_cache, const int32_t* block_tables,
-                                       const int32_t* context_lens, int32_t B, int32_t Hq,
-                                       int32_t Hkv, int32_t D, int32_t block_size,
-                                       int32_t max_blocks, int32_t max_context_len, float scale,
-                                       int32_t partition_size, pa_stream_t stream) {
-  // the workspace this call needs (0 for a single pass), checked before anything
-  // else touches the device: larger than the array is refused
-  if (partition_size < -1 || (partition_size > 0 && partition_size % 16 != 0)) return PA_ERR_SHAPE;
-  const int32_t P = partition_size == -1 && B > 0 && Hkv > 0 && max_context_len > 0
-                        ? pa_decode_partition_size(B, Hkv, max_context_len)
-                        : partition_size;
-  const size_t need = P > 0 && B > 0 && max_context_len > 0
-                          ? pa_decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, P)
-                          : 0;
-  if (need > kScratchBytes) return PA_ERR_WORKSPACE;
-  void* ws = device_scratch();
-  if (ws == nullptr) return PA_ERR_HIP;
-  return pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, D, block_size,
-                   max_blocks, max_context_len, scale, P, ws, kScratchBytes, stream);
-}
+namespace pa {
+void* decode_scratch() { return device_scratch(); }
+}  // namespace pa

@@ -1,4 +1,5 @@
-// Stand-ins for the kernel launchers of libpa, for the CPU-only sanitizer build
+// Stand-ins for the kernel launchers (and the device workspace array) of libpa,
+// for the CPU-only sanitizer build
 // of the host code (pa_api.cpp, block_manager.cpp): every launch reports that no
 // device function is available, so an entry point that got past its host-side
 // validation returns PA_ERR_HIP instead of enqueueing anything.
@@ -9,6 +10,8 @@ namespace pa {
 namespace {
 hipError_t no_device() { return hipErrorInvalidDeviceFunction; }
 }  // namespace
+
+void* decode_scratch() { return nullptr; }  // no device array in the host build
 
 hipError_t launch_cache_store(void*, const void*, const void*, void*, void*, const int32_t*,
                               const int32_t*, const float*, int, int, int, int, hipStream_t) {
