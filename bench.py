@@ -230,14 +230,15 @@ def run_graph(layers, steps, warmup):
 def run_verify(layers, steps, warmup, nq=5):
     """Speculative verification over the same 28 layer caches: nq queries per
     sequence (the last accepted token and nq-1 drafts) through pa_decode_multi
-    with 512-token partitions, one call per layer, back to back (cold caches)."""
+    with the library's partition choice (1024 tokens at this shape), one call per
+    layer, back to back (cold caches)."""
     gen = torch.Generator(device=layers[0].q.device)
     gen.manual_seed(2407)
     calls = []
     for b in layers:
         q = torch.randn((b.B, nq, b.Hq, b.D), generator=gen, device=b.q.device).to(torch.bfloat16)
         calls.append(pa.prepare_decode_multi(q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
-                                             b.scale, b.max_context_len, LONG_P))
+                                             b.scale, b.max_context_len, -1))
 
     def run():
         for c in calls:
@@ -255,7 +256,9 @@ def run_verify(layers, steps, warmup, nq=5):
     kv = W.kv_bytes_logical(layers[0].context_lens.cpu().numpy(), layers[0].Hkv, layers[0].D)
     return {"queries_per_sequence": nq, "us_per_layer_call": round(us, 2),
             "kv_GBps": round(kv / us / 1e3, 1), "pct_of_hbm_peak": round(kv / us / 1e3 / HBM_PEAK_GBPS * 100, 2),
-            "note": "pa_decode_multi, partitions of 512 + combine, 28 layer caches of 16 x 8192 tokens"}
+            "partition_size": 1024,
+            "note": "pa_decode_multi with the library's partition choice (1024 tokens: one chunk of 8 waves "
+                    "per workgroup) + combine, 28 layer caches of 16 x 8192 tokens"}
 
 
 # ---------------------------------------------------------------------------

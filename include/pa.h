@@ -219,8 +219,15 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
  * context_lens    int32 [B]; L_b >= NQ is a device-side precondition
  *                 (a query whose position would be negative sees no key and
  *                 gets zeros); L_b == 0 gives zeros.
+ * partition_size  as for pa_decode, except that -1 (library choice) takes
+ *                 1024 where pa_decode_partition_size gives 512, the rows of a
+ *                 (sequence, KV head) fill two 16-row tiles (NQ * Hq / Hkv > 16)
+ *                 and B * Hkv * ceil(max_context_len / 1024) is at least the
+ *                 device's CU count: partitions of 513 to 1024 tokens run as one
+ *                 chunk of 8 waves per workgroup.
  * other arguments as for pa_decode; the workspace holds fp32 partials
- * [B][NQ][Hq][P][D] followed by log-sum-exps [B][NQ][Hq][P].
+ * [B][NQ][Hq][P][D] followed by log-sum-exps [B][NQ][Hq][P]
+ * (pa_decode_multi_workspace_bytes resolves -1 the same way).
  */
 size_t pa_decode_multi_workspace_bytes(int32_t B, int32_t NQ, int32_t Hq, int32_t Hkv, int32_t D,
                                        int32_t max_context_len, int32_t partition_size);

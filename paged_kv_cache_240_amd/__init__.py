@@ -432,8 +432,8 @@ def prepare_decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale,
     _check(out, "out", torch.bfloat16, 4, dev)
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
-    P = decode_partition_size(B, hkv, max_context_len) if partition_size == -1 else partition_size
-    need = decode_multi_workspace_bytes(B, nq, hq, hkv, d, max_context_len, P) if P > 0 else 0
+    P = int(partition_size)  # -1 is resolved by the library (pa_decode_multi's own rule)
+    need = decode_multi_workspace_bytes(B, nq, hq, hkv, d, max_context_len, P) if P != 0 else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None:

@@ -11,10 +11,13 @@
 // It is the decode kernel's layout with NQ * G (query, head) rows instead of G
 // heads: one workgroup per (sequence, KV head, partition) reads every K/V byte
 // once for all its rows.  Rows r = i * G + h fill up to two 16-row MFMA tiles
-// (CT).  Workgroup = 4 waves; a partition of up to 512 tokens is walked in
-// chunks of 32 blocks, wave w taking blocks w, w+4, ..., w+28, as block pairs
-// in the order K(2j), K(2j+1), V(2j), V(2j+1) through a 4-slot register ring
-// (loads run one pair ahead).  Per pair and row tile:
+// (CT).  A workgroup of NW waves walks its range in chunks of 8 * NW blocks,
+// wave w taking blocks w, w+NW, ..., w+7NW, as block pairs in the order
+// K(2j), K(2j+1), V(2j), V(2j+1) through a 4-slot register ring (loads run one
+// pair ahead).  Partitions of up to 512 tokens are one chunk of 4 waves; those
+// of up to 1024 one chunk of 8 waves (two waves per SIMD at two row tiles,
+// one workgroup per CU); longer ranges repeat 4-wave chunks.  Per pair and row
+// tile:
 //   QK   S^T = K Q^T (v_mfma_f32_16x16x32_bf16, K straight from memory as the
 //        A operand, the tile's query rows as the B operand); keys past the
 //        row's causal limit or the range become -inf by a select.
@@ -38,9 +41,8 @@
 namespace pa {
 namespace {
 
-constexpr int kWaves = 4;
 constexpr int kWaveBlocks = 8;                           // blocks per wave per chunk
-constexpr int kChunkTokens = kWaves * kWaveBlocks * kBlockSize;  // 512
+constexpr int kChunkTokens = 4 * kWaveBlocks * kBlockSize;  // 512: a chunk of 4 waves
 constexpr int kDepth = 4;                                // ring slots: one block pair of K and V
 constexpr float kLazyLog2 = 8.f;                         // reference max may lag by 2^8
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
@@ -62,18 +64,21 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 __host__ __device__ constexpr int step_block(int s) { return 2 * (s / 4) + (s % 2); }
 __host__ __device__ constexpr bool step_is_v(int s) { return (s % 4) >= 2; }
 
-// ONE: the range is a single chunk (partitions of at most 512 tokens): no
-// refills past it.
+// ONE: the range is a single chunk (partitions of at most 64 * NW tokens): no
+// refills past it.  NW: waves per workgroup (4, or 8 for single-chunk
+// partitions of up to 1024 tokens, one workgroup per CU).
 // Two row tiles with a ring that cycles over chunks need more than the 256
 // registers of two waves per SIMD: that variant runs one wave per SIMD.
-template <int D, int G, int CT, bool SPLIT, bool ONE>
-__global__ void __launch_bounds__(256, (CT == 2 && !ONE) ? 1 : 2)
+template <int D, int G, int CT, bool SPLIT, bool ONE, int NW>
+__global__ void __launch_bounds__(64 * NW, (CT == 2 && !ONE) || NW == 8 ? 1 : 2)
 decode_multi_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
                     const int32_t* __restrict__ context_lens, int NQ, int Hkv, int max_blocks,
                     float scale_log2, int part_tokens, int num_parts, uint16_t* __restrict__ out,
                     float* __restrict__ o_part, float* __restrict__ lse) {
   static_assert(CT == 1 || CT == 2, "one or two 16-row tiles");
+  constexpr int kWaves = NW;
+  constexpr int kChunk = NW * kWaveBlocks * kBlockSize;  // tokens of one chunk
   constexpr int KS = D / 32;    // QK k-steps over the head dimension
   constexpr int DPL = D / 16;   // PV: dims per lane = output tiles of 16 columns
   constexpr int HALF = DPL / 2; // dwords of one V row piece
@@ -152,14 +157,14 @@ decode_multi_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
   const int64_t head_off = (int64_t)g * kBlockSize * D;
   const int64_t blk_stride = (int64_t)Hkv * kBlockSize * D;
-  const int nchunks = ONE ? 1 : (t_end - t_begin + kChunkTokens - 1) / kChunkTokens;
+  const int nchunks = ONE ? 1 : (t_end - t_begin + kChunk - 1) / kChunk;
   const int last_lb = (t_end - 1) / kBlockSize;
   const int lane_k = col * D + quad * 8;
   const int lane_v = col * DPL;
   const uint4 ones = make_uint4(kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2);
 
   auto fetch_entries = [&](int c) -> int {
-    const int lb = (t_begin + c * kChunkTokens) / kBlockSize + wave + kWaves * (lane & 7);
+    const int lb = (t_begin + c * kChunk) / kBlockSize + wave + kWaves * (lane & 7);
     return bt_row[min(lb, last_lb)];
   };
   // ring step `step` of the chunk whose entries are `ent`; `left` = rows of that block in range
@@ -194,15 +199,15 @@ decode_multi_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
   int ent_cur = lb_spec <= last_lb ? ent_spec : ent_first;  // == fetch_entries(0)
   int ent_nxt = ONE ? 0 : fetch_entries(nchunks > 1 ? 1 : 0);
-  const int nt0 = min(kChunkTokens, t_end - t_begin);
+  const int nt0 = min(kChunk, t_end - t_begin);
   uint32_t ring[kDepth][SLOT];
 #pragma unroll
   for (int s = 0; s < kDepth; ++s) load_step(ring[s], ent_cur, s, rows_left(nt0, s));
 
   for (int c = 0; c < nchunks; ++c) {
-    const int c0 = t_begin + c * kChunkTokens;
-    const int nt = min(kChunkTokens, t_end - c0);
-    const int nt_next = min(kChunkTokens, t_end - c0 - kChunkTokens);
+    const int c0 = t_begin + c * kChunk;
+    const int nt = min(kChunk, t_end - c0);
+    const int nt_next = min(kChunk, t_end - c0 - kChunk);
     floatx4_t st[2][CT];  // raw scores of the pair: keys 4*quad+e of its two blocks
     uint4 pa[CT];         // bf16 probabilities of the pair (PV A operand)
 
@@ -363,13 +368,16 @@ hipError_t launch_g(void* out, float* o_part, float* lse, const void* q, const v
   if (P > 0) {
     const int np = (mcl + P - 1) / P;
     if (P <= kChunkTokens)
-      hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, true, true>), dim3(np, Hkv, B), dim3(256), 0,
+      hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, true, true, 4>), dim3(np, Hkv, B), dim3(256), 0,
+                         stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, P, np, oo, o_part, lse);
+    else if (P <= 2 * kChunkTokens)
+      hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, true, true, 8>), dim3(np, Hkv, B), dim3(512), 0,
                          stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, P, np, oo, o_part, lse);
     else
-      hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, true, false>), dim3(np, Hkv, B), dim3(256), 0,
+      hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, true, false, 4>), dim3(np, Hkv, B), dim3(256), 0,
                          stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, P, np, oo, o_part, lse);
   } else {
-    hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, false, false>), dim3(1, Hkv, B), dim3(256), 0,
+    hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, false, false, 4>), dim3(1, Hkv, B), dim3(256), 0,
                        stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, 0, 1, oo, o_part, lse);
   }
   return hipGetLastError();

@@ -80,6 +80,21 @@ int32_t resolve_partition(int32_t partition_size, int32_t B, int32_t Hkv, int32_
   return partition_size == -1 ? pa_decode_partition_size(B, Hkv, max_context_len) : partition_size;
 }
 
+// partition_size -1 for the multi-query decode: the decode choice, except that
+// rows filling two 16-row tiles (NQ * G > 16) move from 512 to 1024 tokens while
+// the 1024-token grid still gives every CU a workgroup.  A 1024-token partition
+// runs as one chunk of 8 waves, two per SIMD, and halves the partials to
+// reduce: measured 29.9 against 33.1 us per call on 16 x 8192 tokens, NQ = 5.
+int32_t resolve_multi_partition(int32_t partition_size, int32_t B, int32_t NQ, int32_t Hq,
+                                int32_t Hkv, int32_t max_context_len) {
+  if (partition_size != -1) return partition_size;
+  const int32_t P = pa_decode_partition_size(B, Hkv, max_context_len);
+  if (P == 512 && Hkv > 0 && (int64_t)NQ * (Hq / Hkv) > 16 &&
+      (int64_t)B * Hkv * ceil_div(max_context_len, 1024) >= device_cu_count())
+    return 1024;
+  return P;
+}
+
 }  // namespace
 
 extern "C" {
@@ -379,8 +394,9 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
 
 size_t pa_decode_multi_workspace_bytes(int32_t B, int32_t NQ, int32_t Hq, int32_t Hkv, int32_t D,
                                        int32_t max_context_len, int32_t partition_size) {
-  if (NQ <= 0) return 0;
-  const size_t per_query = pa_decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, partition_size);
+  if (NQ <= 0 || B < 0 || Hq <= 0 || Hkv <= 0 || max_context_len < 0) return 0;
+  const int32_t P = resolve_multi_partition(partition_size, B, NQ, Hq, Hkv, max_context_len);
+  const size_t per_query = pa_decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, P);
   return per_query * (size_t)NQ;
 }
 
@@ -397,7 +413,7 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
   if (NQ <= 0) return PA_ERR_SHAPE;
   if ((int64_t)NQ * (Hq / Hkv) > 32) return PA_ERR_UNSUPPORTED;
   if (partition_size < -1 || (partition_size > 0 && partition_size % 16 != 0)) return PA_ERR_SHAPE;
-  const int32_t P = resolve_partition(partition_size, B, Hkv, max_context_len);
+  const int32_t P = resolve_multi_partition(partition_size, B, NQ, Hq, Hkv, max_context_len);
   if (B == 0) return PA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (P == 0 || max_context_len == 0)

@@ -170,6 +170,21 @@ def test_decode_multi_workspace_is_per_query_decode_workspace():
     assert lib.pa_decode_multi_workspace_bytes(4, 0, 12, 2, 128, 100, 16) == 0
 
 
+def test_decode_multi_library_partition_choice():
+    # -1: decode's choice, except 512 -> 1024 when two row tiles (NQ * G > 16) still give every CU
+    # a workgroup at 1024 tokens (no GPU here: the library assumes 256 CUs)
+    lib = pa.load()
+    assert lib.pa_decode_partition_size(16, 2, 8192) == 512
+    assert lib.pa_decode_multi_workspace_bytes(16, 5, 12, 2, 128, 8192, -1) == \
+        lib.pa_decode_multi_workspace_bytes(16, 5, 12, 2, 128, 8192, 1024)
+    # one 16-row tile (NQ * G <= 16): decode's choice
+    assert lib.pa_decode_multi_workspace_bytes(16, 2, 12, 2, 128, 8192, -1) == \
+        lib.pa_decode_multi_workspace_bytes(16, 2, 12, 2, 128, 8192, 512)
+    # a 1024-token grid below the CU count: decode's choice
+    assert lib.pa_decode_multi_workspace_bytes(8, 5, 12, 2, 128, 8192, -1) == \
+        lib.pa_decode_multi_workspace_bytes(8, 5, 12, 2, 128, 8192, lib.pa_decode_partition_size(8, 2, 8192))
+
+
 def _copy(**kw):
     a = dict(kc=P, vc=P, src=P, dst=P, n=4, Hkv=2, D=128, bs=16, nb=64)
     a.update(kw)

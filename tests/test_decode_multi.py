@@ -36,7 +36,8 @@ def _run(pa, b, nq, partitions, label):
 
 
 def test_spec_verify_workload(gpu):
-    # 16 sequences x 8192 tokens, 5 queries each (4 drafts), Qwen head shape, 512-token partitions
+    # 16 sequences x 8192 tokens, 5 queries each (4 drafts), Qwen head shape; 512-token partitions
+    # and the library choice (1024: one 8-wave chunk per workgroup)
     _run(gpu, W.spec_verify(), 5, [512, -1], "spec verify 16x8192")
 
 
@@ -55,7 +56,7 @@ def test_head_shapes(gpu, D, G, Hkv, nq):
     lens = [nq, 40, 77, 300, 1025]
     b = W.verify_batch(lens, nq, G * Hkv, Hkv, D, 256, 3400 + 7 * G + nq + D, theta=1e4,
                        poison=True, table_fill=W.INT32_MIN)
-    _run(gpu, b, nq, [0, 64, 512], f"G={G} Hkv={Hkv} nq={nq} D={D}")
+    _run(gpu, b, nq, [0, 64, 512, 768, 1024], f"G={G} Hkv={Hkv} nq={nq} D={D}")
 
 
 def test_wide_score_range(gpu):
