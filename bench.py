@@ -25,6 +25,7 @@ committed files only):
     python bench.py --mode decode-kernel   # 3 x 28 launches of the step's partition kernel
     python bench.py --mode partition-kernel  # 3 x 28 launches of the unfused partition kernel
     python bench.py --mode prefill-kernel  # 20 launches of the prefill kernel only
+    python bench.py --mode cb-cold  # continuous-batching step, 10 cold calls of each path
     python bench.py --mode copy-calibration  # torch copy of 1 GiB (FETCH/WRITE_SIZE scale)
     python bench.py --mode write-traffic --pmc F_STEP W_STEP F_COPY W_COPY
         # profiles/decode_partitions_traffic.json from the four counter folders
@@ -762,7 +763,7 @@ def main():
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--mode", default="bench",
                     choices=["bench", "decode-kernel", "partition-kernel", "prefill-kernel",
-                             "copy-calibration", "write-traffic"])
+                             "cb-cold", "copy-calibration", "write-traffic"])
     ap.add_argument("--pmc", nargs=4, metavar=("FETCH_STEP", "WRITE_STEP", "FETCH_COPY", "WRITE_COPY"),
                     help="write-traffic: the four rocprofv3 --pmc output folders")
     args = ap.parse_args()
@@ -803,6 +804,28 @@ def main():
         _sync()
         nbytes = step_kernel_bytes(Ls[0]) if args.mode == "decode-kernel" else partition_kernel_bytes(Ls[0])
         print(json.dumps({"mode": args.mode, "launches": 3 * len(Ls), "bytes_per_launch": nbytes}))
+        return
+    if args.mode == "cb-cold":
+        # the continuous-batching step, cold: 10 calls of pa_decode (library partition), then 10
+        # of pa_decode_shared_prefix, each after a 1 GiB rewrite (for counter and trace runs)
+        b = W.cb_step(device=dev)
+        scrub = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+        P = pa.decode_partition_size(b.B, b.Hkv, b.max_context_len)
+        dec = pa.prepare_decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale,
+                                b.max_context_len, P)
+        prefix = torch.zeros(b.B, dtype=torch.int32, device=dev)
+        prefix[:32] = 2000
+        sp = pa.prepare_decode_shared_prefix(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
+                                             torch.tensor([0, 32], dtype=torch.int32, device=dev), prefix,
+                                             b.scale, b.max_context_len, 32, 2000,
+                                             int((b.context_lens - prefix).max()), -1)
+        for fn in (dec, sp):
+            for _ in range(10):
+                scrub.add_(1)
+                _sync()
+                fn()
+                _sync()
+        print(json.dumps({"mode": "cb-cold", "calls": [10, 10], "partition_size": P}))
         return
     if args.mode == "prefill-kernel":
         b = W.chunked_prefill(device=dev)
