@@ -292,14 +292,21 @@ pa_status pa_decode_step_partitions(float* o_part, float* lse, const void* q, co
  * Decode with shared prefixes read once ([mini-llm] §3.4: full blocks shared
  * by several sequences, ref_count > 1; [Pico-vLLM] §3: requests sharing a
  * system prompt).  The same result as pa_decode (up to rounding order), but
- * the keys of a prefix shared by a group of sequences are read once for the
- * whole group: the group's queries (every sequence and head) attend each
- * partition of the prefix (128 to 1024 tokens, the library's choice) together
- * on the matrix cores, each sequence's own split-K partitions cover only its
- * tokens after the prefix, and one log-sum-exp reduce merges both sets of
- * partials.  It pays when many sequences share a long prefix (measured: 1.6x
- * pa_decode for 128 sequences sharing 4096 tokens); for a few sequences on a
- * prefix that stays in the last-level cache, pa_decode is faster.
+ * the keys of a prefix shared by a group of sequences are read once for
+ * several sequences: each sequence's own split-K partitions cover only its
+ * tokens after the prefix, and one log-sum-exp reduce merges them with the
+ * prefix partials.  Two ways, the library's choice:
+ *   - one partition launch: work items of up to 32 (sequence, head) rows,
+ *     32 / G sequences of a group over one 512-token partition of their prefix
+ *     or one sequence's heads over one partition of its suffix; taken when
+ *     there is a prefix, the suffix partitions are at most 512 tokens and the
+ *     prefix items number at most one per CU;
+ *   - otherwise the group's queries (every sequence and head, 128 rows per
+ *     workgroup) attend each partition of the prefix (128 to 1024 tokens)
+ *     together on the matrix cores, then the suffix partitions, then the reduce.
+ * It pays when many sequences share a long prefix (measured: 2.0x pa_decode
+ * for 128 sequences sharing 4096 tokens); for a few sequences on a prefix that
+ * stays in the last-level cache, pa_decode is faster.
  *
  * group_start     int32 [num_groups + 1], device memory: group i is sequences
  *                 group_start[i] .. group_start[i+1]-1 (contiguous, ascending,

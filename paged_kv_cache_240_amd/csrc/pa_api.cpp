@@ -294,6 +294,8 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
 namespace {
 constexpr int kPrefixPartTokens = 128;  // smallest shared-prefix partition: a key tile per half
 constexpr int kMaxCascadeSlots = 64;
+constexpr int kOneLaunchPrefix = 512;   // prefix partition of the one-launch path
+constexpr int kOneLaunchMaxItems = 1;   // its prefix items per CU, at most
 
 int32_t cascade_slots(int32_t max_suffix, int32_t P, int32_t max_prefix, int32_t Pg = kPrefixPartTokens) {
   return (int32_t)(ceil_div(max_suffix, P) + ceil_div(max_prefix, Pg));
@@ -363,6 +365,38 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
     P = std::max<int32_t>(P, 64);
   }
   const int32_t suffix_slots = (int32_t)ceil_div(suf, P);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // One partition launch for prefixes and suffixes together: prefix items of up
+  // to 32 rows (32 / G sequences of a group), prefix partitions of kOneLaunchPrefix
+  // tokens; taken when there is a prefix, the suffix partitions are single
+  // chunks and the prefix items stay within kOneLaunchMaxItems per CU.  (With no
+  // prefix the suffix pass below is pa_decode's own partition kernel.)
+  {
+    const int32_t Pc = kOneLaunchPrefix;
+    const int64_t sub = 32 / (Hq / Hkv);
+    const int64_t pre_items = (num_groups > 0 && max_prefix > 0)
+                                  ? (int64_t)num_groups * ceil_div(std::max(max_group_size, 1), sub) *
+                                        ceil_div(max_prefix, Pc) * Hkv
+                                  : 0;
+    const int32_t slots = cascade_slots(suf, P, max_prefix, Pc);
+    if (pre_items > 0 && P <= 512 && slots <= kMaxCascadeSlots &&
+        pre_items <= kOneLaunchMaxItems * device_cu_count()) {
+      const size_t need = (size_t)((int64_t)B * Hq * slots * (D + 1) * (int64_t)sizeof(float));
+      if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+      float* o_part = static_cast<float*>(workspace);
+      float* lse = o_part + (int64_t)B * Hq * slots * D;
+      hipError_t e = pa::launch_cascade_partitions(o_part, lse, q, k_cache, v_cache, block_tables,
+                                                   context_lens, group_start, prefix_lens, B,
+                                                   num_groups, max_group_size, max_prefix, Pc, suf,
+                                                   P, suffix_slots, slots, Hq, Hkv, D, max_blocks,
+                                                   scale, s);
+      if (e != hipSuccess) return PA_ERR_HIP;
+      return from_hip(pa::launch_decode_combine_cascade(out, o_part, lse, context_lens, prefix_lens,
+                                                        B, Hq, D, slots, P, suffix_slots, Pc, s));
+    }
+  }
+  // Otherwise the group pass on the matrix cores (128-row workgroups), then the
+  // suffix partitions, then the reduce.
   // row blocks of 128 (sequence, head) rows per group, times KV heads and groups
   const int32_t row_blocks = (int32_t)(ceil_div((int64_t)std::max(max_group_size, 1) * (Hq / Hkv), 128) *
                                        Hkv * std::max(num_groups, 1));
@@ -374,7 +408,6 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
   // the workspace query sizes for the smallest prefix partition: always enough
   const size_t need = (size_t)((int64_t)B * Hq * slots * (D + 1) * (int64_t)sizeof(float));
   if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   float* o_part = static_cast<float*>(workspace);
   float* lse = o_part + (int64_t)B * Hq * slots * D;
   const int32_t slot0 = suffix_slots;

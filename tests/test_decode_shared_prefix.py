@@ -91,3 +91,13 @@ def test_large_group_longer_prefix_partitions(gpu):
     b = W.decode_batch(lens, 12, 2, 128, 128 * 6 + 256 + 64, 6203, theta=1e6,
                        shared_prefix=(list(range(128)), 256))
     _run(gpu, b, [(0, 128, 4096)], [64], "128 x 4096")
+
+
+def test_large_group_eight_heads_head_dim_64(gpu):
+    # 96 sequences (G = 8, D = 64) on a 6144-token prefix: 288 prefix items of four
+    # sequences at 512 tokens would not fit one per CU, so the group pass runs on the
+    # matrix cores (the 128-row workgroups), then the suffixes, then the reduce
+    lens = [6144 + 16 + 5 * (i % 7) for i in range(96)]
+    b = W.decode_batch(lens, 8, 1, 64, 96 * 3 + 384 + 64, 6204, theta=1e6,
+                       shared_prefix=(list(range(96)), 384))
+    _run(gpu, b, [(0, 96, 6144)], [64, -1], "96 x 6144, G=8, D=64")
