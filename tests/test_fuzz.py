@@ -63,7 +63,7 @@ def test_decode_and_decode_step(gpu, case):
     assert _same_bits(o2, out) and _same_bits(g2.k_cache, g.k_cache) and _same_bits(g2.v_cache, g.v_cache)
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(12))
 def test_multi_query_decode(gpu, case):
     rng = np.random.default_rng(8200 + case)
     D, G, Hkv = _shape(rng)
@@ -71,7 +71,7 @@ def test_multi_query_decode(gpu, case):
     nq = min(nq, 6)
     B = int(rng.integers(1, 5))
     lens = [max(nq, _length(rng, 1500)) for _ in range(B)]
-    P = int(rng.choice([0, -1, 64 * int(rng.integers(1, 9))]))
+    P = int(rng.choice([0, -1, 64 * int(rng.integers(1, 17))]))  # up to 1024: the 8-wave chunks
     print(f"multi case {case}: D={D} G={G} Hkv={Hkv} nq={nq} lens={lens} P={P}", flush=True)
     b = W.verify_batch(lens, nq, G * Hkv, Hkv, D, sum(-(-L // 16) for L in lens) + 8, 8300 + case,
                        poison=True, table_fill=W.INT32_MIN)
@@ -84,6 +84,54 @@ def test_multi_query_decode(gpu, case):
                            g.context_lens, g.scale, g.max_context_len, partition_size=P)
     torch.cuda.synchronize()
     assert_attention_close(out, ref, f"multi case {case}")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_shared_prefix_decode(gpu, case):
+    # random groups of sequences sharing whole-block prefixes, sequences in no group,
+    # random suffix partitions: the one-launch form or the matrix-core group pass
+    rng = np.random.default_rng(8600 + case)
+    D, G, Hkv = _shape(rng)
+    B = int(rng.integers(2, 13))
+    ngroups = int(rng.integers(1, 4))
+    cuts = sorted(int(x) for x in rng.choice(np.arange(1, B), size=min(ngroups, B - 1), replace=False))
+    bounds = [0] + cuts
+    groups, prefix = [], [0] * B
+    for gi in range(len(bounds) - 1 + (1 if rng.integers(2) else 0)):
+        first = bounds[gi]
+        end = bounds[gi + 1] if gi + 1 < len(bounds) else B
+        if end - first < 1 or rng.integers(4) == 0:
+            continue                                  # sometimes leave a run ungrouped
+        pre = 16 * int(rng.integers(1, 80))
+        groups.append((first, end, pre))
+        for sidx in range(first, end):
+            prefix[sidx] = pre
+    lens = [prefix[i] + _length(rng, 700) for i in range(B)]
+    P = int(rng.choice([-1, 16 * int(rng.integers(1, 33))]))
+    print(f"shared-prefix case {case}: D={D} G={G} Hkv={Hkv} groups={groups} lens={lens} P={P}",
+          flush=True)
+    nb = sum(-(-L // 16) for L in lens) + 8
+    b = W.decode_batch(lens, G * Hkv, Hkv, D, nb, 8700 + case, theta=1e4, poison=True,
+                       table_fill=W.INT32_MIN)
+    bt = b.block_tables.clone()
+    for first, end, pre in groups:
+        for sidx in range(first + 1, end):
+            bt[sidx, :pre // 16] = bt[first, :pre // 16]
+    b.block_tables = bt
+    q_ref, kc_ref, vc_ref = oracle_store(b)
+    ref = oracle_decode(q_ref, kc_ref, vc_ref, b)
+    g = b.to("cuda")
+    gpu_store(gpu, g)
+    start = torch.tensor([f for f, _, _ in groups] + [groups[-1][1]] if groups else [0],
+                         dtype=torch.int32, device="cuda")
+    pre_t = torch.tensor(prefix, dtype=torch.int32, device="cuda")
+    max_group = max([e - f for f, e, _ in groups], default=1)
+    out = gpu.decode_shared_prefix(g.q, g.k_cache, g.v_cache, g.block_tables, g.context_lens,
+                                   start if groups else None, pre_t, g.scale, g.max_context_len,
+                                   max_group, max(prefix), max(L - p for L, p in zip(lens, prefix)),
+                                   partition_size=P)
+    torch.cuda.synchronize()
+    assert_attention_close(out, ref, f"shared-prefix case {case}")
 
 
 @pytest.mark.parametrize("case", range(8))
