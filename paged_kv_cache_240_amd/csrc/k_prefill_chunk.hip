@@ -9,15 +9,16 @@
 //
 // Rows are (position, head) pairs of one (sequence, KV head), position-major
 // (r = pos * G + h), so the G query heads sharing a KV head share every K/V
-// tile.  A workgroup takes 96 rows and all the keys they can see; its 8 waves
-// form 4 key ranges ("quarters", consecutive runs of 32-key steps) of 2 waves,
-// and each wave owns 48 rows (three 16-row tiles) over its quarter's keys.
+// tile.  A workgroup takes 96 rows and all the keys they can see; its 12 waves
+// form 4 key ranges ("quarters", consecutive runs of 32-key steps) of 3 waves,
+// and each wave owns 32 rows (two 16-row tiles) over its quarter's keys.
 // 96-row workgroups make one workgroup per compute unit on the chunked-prefill
-// shape (32 per (sequence, KV head), 8 pairs), and 48 rows per wave let every
-// K/V operand read from LDS feed three matrix products.
+// shape (32 per (sequence, KV head), 8 pairs); 32 rows per wave keep a wave
+// within 170 registers, so three waves share each SIMD and cover each other's
+// latency, and every K/V operand read from LDS feeds two matrix products.
 //
 // Per 32-key step (two 16-token blocks) and quarter:
-//   load  each of the quarter's waves brings one block's K and V rows straight
+//   load  two of the quarter's waves each bring one block's K and V rows straight
 //         from global memory into LDS (global_load_lds_dwordx4: lane i of an
 //         instruction lands at byte 16*i of its 1 KiB destination), so no
 //         register staging; a lane fetches the 16-byte chunk that the XOR
@@ -57,11 +58,11 @@ typedef short shortx4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kQuarters = 4;                       // key ranges per workgroup
-constexpr int kWavesPerQ = 2;                      // waves sharing a key range
-constexpr int kWaves = kQuarters * kWavesPerQ;     // 8
-constexpr int kThreads = 64 * kWaves;              // 512
-constexpr int kRowTiles = 3;                       // 16-row tiles per wave
-constexpr int kRowsPerWave = 16 * kRowTiles;       // 48
+constexpr int kWavesPerQ = 3;                      // waves sharing a key range
+constexpr int kWaves = kQuarters * kWavesPerQ;     // 12
+constexpr int kThreads = 64 * kWaves;              // 768
+constexpr int kRowTiles = 2;                       // 16-row tiles per wave
+constexpr int kRowsPerWave = 16 * kRowTiles;       // 32
 constexpr int kRowsPerWG = kWavesPerQ * kRowsPerWave;  // 96
 constexpr int kStepKeys = 2 * kBlockSize;          // 32 keys per step
 constexpr float kLazyLog2 = 8.f;                   // reference max may lag by 2^8
@@ -156,7 +157,7 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int r = roww0 + rt * 16 + col;
     lim[rt] = L - C + (r < nrows ? r / G : 0);
   }
-  // B operands of QK: the wave's 48 query rows, 8 dims per k-step (rows past the
+  // B operands of QK: the wave's 32 query rows, 8 dims per k-step (rows past the
   // chunk read its first row: finite, never written out)
   bf16x8_t qb[kRowTiles][KS];
 #pragma unroll
@@ -179,7 +180,7 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     comp_end = min(max(lim_hi / kStepKeys + 1, s_begin), s_end);
   }
 
-  // ---- direct loads: this wave brings block w of each step of its quarter ----------
+  // ---- direct loads: waves 0 and 1 of the quarter bring blocks 0 and 1 of each step ----
   // Instruction j covers key rows j*KPI .. j*KPI + KPI-1 of the block (1 KiB of
   // LDS); lane i fills slot i % NCH of row j*KPI + i / NCH with the chunk that
   // slot holds, chunk = slot ^ mask(row of the step).  With w*16 + row as the
@@ -193,8 +194,9 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   const uint32_t kl = (uint32_t)((lane / LY::NCH) * LY::ROW + (((lane % LY::NCH) ^ (lane >> 4)) << 4));
   const uint32_t v0 = (uint32_t)(((lane % LY::NCH) ^ (2 * (lane >> 4))) << 4);
   const uint32_t vl = (uint32_t)((lane / LY::NCH) * LY::ROW) + v0;
-  auto entry = [&](int s) { return bt_row[min(s * 2 + w, nblk - 1)]; };
+  auto entry = [&](int s) { return bt_row[min(s * 2 + min(w, 1), nblk - 1)]; };
   auto issue = [&](int s, int e, unsigned char* dst) {
+    if (w >= 2) return;  // two blocks per step: waves 0 and 1 load them
     const int tok0 = s * kStepKeys + w * kBlockSize;
     const char* kb = reinterpret_cast<const char*>(k_cache + (int64_t)e * blk_stride + head_off);
     const char* vb = reinterpret_cast<const char*>(v_cache + (int64_t)e * blk_stride + head_off);
@@ -367,7 +369,7 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     l += swap16(l);
     lsum[rt] = l + swap32(l);
   }
-  // a wave's state in merge slot `slot` (0, 1 in buf_a; 2, 3 in buf_b): [k][64 lanes]
+  // a wave's state in merge slot `slot` (0 .. kWavesPerQ-1 in buf_a, the next kWavesPerQ in buf_b): [k][64 lanes]
   auto at = [&](int slot, int k) -> float& {
     float* mg = reinterpret_cast<float*>(slot < kWavesPerQ ? &buf_a[0][0] : &buf_b[0][0]);
     return mg[((slot % kWavesPerQ) * MERGE + k) * 64 + lane];
