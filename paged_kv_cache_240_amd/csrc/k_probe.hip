@@ -8,7 +8,7 @@
 // loads cannot be removed; one sum per workgroup is written.
 // gather_read: the buffer as 4 KiB tiles visited in a scrambled order (tile t
 // at (t * 0x9E3779B1) mod ntiles, a bijection for a power-of-two count), each
-// wave loading its 8 tiles with all 32 of its 16-byte loads in flight, then
+// wave loading its 4 tiles with all 16 of its 16-byte loads in flight, then
 // leaving: one pass, the access granularity and the scattered placement of a
 // paged K/V read.  Sums as stream_read.
 // mfma_bf16: every wave runs `iters` rounds of four independent
@@ -55,7 +55,7 @@ stream_read_kernel(const uint4* __restrict__ buf, int64_t n16, uint32_t* __restr
 }
 
 constexpr int kTileWords16 = 4096 / 16;  // 16-byte pieces of a 4 KiB tile
-constexpr int kGatherTiles = 8;           // tiles per wave
+constexpr int kGatherTiles = 4;           // tiles per wave (the fastest one-launch read of a sweep over 2, 4, 8, 16)
 
 __global__ void __launch_bounds__(kProbeThreads)
 gather_read_kernel(const uint4* __restrict__ buf, int64_t ntiles, uint32_t* __restrict__ sums) {

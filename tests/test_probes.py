@@ -26,14 +26,14 @@ def test_stream_read_sees_every_word_once(gpu, nbytes, grid):
 @pytest.mark.parametrize("nbytes", [4096, 8192, 16384, 1 << 20, 1 << 24])
 def test_gather_read_sees_every_word_once(gpu, nbytes):
     """Every 4 KiB tile is visited once under the scrambled order (sizes below and
-    above one wave's 8 tiles and one workgroup's 32)."""
+    above one wave's 4 tiles and one workgroup's 16)."""
     g = torch.Generator().manual_seed(nbytes + 1)
     words = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32)
     want = int(words.numpy().view(np.uint32).astype(np.uint64).sum() % (1 << 32))
     call = probes.prepare_probe_gather_read(words.cuda())
     sums = call()
     torch.cuda.synchronize()
-    assert sums.numel() == max(1, nbytes // 4096 // 32)
+    assert sums.numel() == max(1, nbytes // 4096 // 16)
     got = int(sums.cpu().numpy().view(np.uint32).astype(np.uint64).sum() % (1 << 32))
     assert got == want
 
