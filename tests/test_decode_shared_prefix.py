@@ -66,7 +66,7 @@ def test_several_groups(gpu, D, G):
     Hkv = 2 if G <= 4 else 1
     b = W.decode_batch(lens, G * Hkv, Hkv, D, 512, 6100 + 10 * G + D, theta=1e4, poison=True,
                        table_fill=W.INT32_MIN)
-    _run(gpu, b, groups, [16, 64, 512, -1], f"G={G} D={D}")
+    _run(gpu, b, groups, [16, 64, 512, 1024, -1], f"G={G} D={D}")  # 1024: the three-launch path
 
 
 def test_without_groups_equals_decode(gpu):
