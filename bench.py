@@ -25,6 +25,7 @@ committed files only):
     python bench.py --mode decode-kernel   # 3 x 28 launches of the step's partition kernel
     python bench.py --mode partition-kernel  # 3 x 28 launches of the unfused partition kernel
     python bench.py --mode prefill-kernel  # 20 launches of the prefill kernel only
+    python bench.py --mode verify-kernel  # 3 x 28 calls of pa_decode_multi (5 queries per sequence)
     python bench.py --mode cb-cold  # continuous-batching step, 10 cold calls of each path
     python bench.py --mode copy-calibration  # torch copy of 1 GiB (FETCH/WRITE_SIZE scale)
     python bench.py --mode write-traffic --pmc F_STEP W_STEP F_COPY W_COPY
@@ -763,7 +764,7 @@ def main():
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--mode", default="bench",
                     choices=["bench", "decode-kernel", "partition-kernel", "prefill-kernel",
-                             "cb-cold", "copy-calibration", "write-traffic"])
+                             "verify-kernel", "cb-cold", "copy-calibration", "write-traffic"])
     ap.add_argument("--pmc", nargs=4, metavar=("FETCH_STEP", "WRITE_STEP", "FETCH_COPY", "WRITE_COPY"),
                     help="write-traffic: the four rocprofv3 --pmc output folders")
     args = ap.parse_args()
@@ -804,6 +805,24 @@ def main():
         _sync()
         nbytes = step_kernel_bytes(Ls[0]) if args.mode == "decode-kernel" else partition_kernel_bytes(Ls[0])
         print(json.dumps({"mode": args.mode, "launches": 3 * len(Ls), "bytes_per_launch": nbytes}))
+        return
+    if args.mode == "verify-kernel":
+        # speculative verification as the bench times it: pa_decode_multi (5 queries per
+        # sequence, the library's partition choice) over the 28 layer caches, 3 times
+        layers = make_long_layers(args.layers, dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(2407)
+        calls = []
+        for b in layers:
+            q = torch.randn((b.B, 5, b.Hq, b.D), generator=gen, device=dev).to(torch.bfloat16)
+            calls.append(pa.prepare_decode_multi(q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
+                                                 b.scale, b.max_context_len, -1))
+        _sync()
+        for _ in range(3):
+            for c in calls:
+                c()
+        _sync()
+        print(json.dumps({"mode": "verify-kernel", "calls": 3 * len(calls)}))
         return
     if args.mode == "cb-cold":
         # the continuous-batching step, cold: 10 calls of pa_decode (library partition), then 10
