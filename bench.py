@@ -52,7 +52,7 @@ import workloads as W  # noqa: E402
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 LONG_P = W.LONG_PARTITION
-STEP_KERNEL = "decode_kernel<128, 6, true, true, true, 8>"
+STEP_KERNEL = "decode_kernel<128, 6, true, true, true, 8, false>"
 
 
 def _sync():
@@ -401,9 +401,20 @@ def run_context(device):
         "per_call_cold": cold_sp,
         "kv_unique_GBps_cold": round(unique / cold_sp["median_us"] / 1e3, 1),
         "unique_frac_of_hbm_peak_cold": round(unique / cold_sp["median_us"] / 1e3 / HBM_PEAK_GBPS, 4),
-        "note": "pa_decode_shared_prefix: the group's queries attend the shared prefix once "
-                "(prefix partitions on the matrix cores), suffixes by split-K, one reduce; at this "
-                "size (32 sequences, 2 MB of prefix that stays in the last-level cache) pa_decode is faster"}
+        "note": "pa_decode_shared_prefix: one partition launch of prefix items (2 sequences x 6 heads "
+                "over 512 prefix tokens) and suffix items, then one reduce; at this size (32 sequences, "
+                "2 MB of prefix) pa_decode is faster"}
+    # the floor of the cold protocol: a one-element add, and pa_decode on a 4-sequence batch of
+    # the same shape (two sequences on a 2000-token prefix + 16 tokens, two of 64 tokens)
+    tiny = torch.zeros(1, device=device)
+    fb = W.decode_batch([2016, 2016, 64, 64], W.QWEN_HQ, W.QWEN_HKV, W.QWEN_D, 512, 9, theta=1e6,
+                        shared_prefix=([0, 1], 125), device=device)
+    dec_f = pa.prepare_decode(fb.q, fb.k_cache, fb.v_cache, fb.block_tables, fb.context_lens, fb.scale,
+                              fb.max_context_len, partition_size=P)
+    res["cold_protocol_floor"] = {"one_element_add_us": time_each(lambda: tiny.add_(1), 50, scrub)["median_us"],
+                                  "pa_decode_4_sequences_us": time_each(dec_f, 50, scrub)["median_us"],
+                                  "note": "the same event window after the same 1 GiB rewrite, on "
+                                          "launches with next to no bytes"}
     # many sequences on one long prefix: 128 x (4096 shared + 128 own) tokens
     lens = [4096 + 128] * 128
     bb = W.decode_batch(lens, W.QWEN_HQ, W.QWEN_HKV, W.QWEN_D, 128 * 8 + 256 + 64, 2414, theta=1e6,
@@ -927,7 +938,8 @@ def main():
                    key=lambda r: r[0]["per_call_cold"]["median_us"])
         line["cb_step_cold"] = {"entry_point": best[1], "us": best[0]["per_call_cold"]["median_us"],
                                 "kv_unique_bytes": cb["kv_unique_bytes"],
-                                "unique_frac_of_hbm_peak": best[0]["unique_frac_of_hbm_peak_cold"]}
+                                "unique_frac_of_hbm_peak": best[0]["unique_frac_of_hbm_peak_cold"],
+                                "protocol_floor": line["context"]["cold_protocol_floor"]}
         kv_layer = W.kv_bytes_logical(layers[0].context_lens.cpu().numpy(), layers[0].Hkv, layers[0].D)
         dc = line["device_ceilings"] = run_ceilings(dev, kv_layer)
         line["roofline"]["frac_of_measured_read"] = round(line["roofline"]["achieved"] / dc["read_ceiling_GBps"], 4)

@@ -296,9 +296,9 @@ pa_status pa_decode_step_partitions(float* o_part, float* lse, const void* q, co
  * several sequences: each sequence's own split-K partitions cover only its
  * tokens after the prefix, and one log-sum-exp reduce merges them with the
  * prefix partials.  Two ways, the library's choice:
- *   - one partition launch: work items of up to 32 (sequence, head) rows,
- *     32 / G sequences of a group over one 512-token partition of their prefix
- *     or one sequence's heads over one partition of its suffix; taken when
+ *   - one partition launch: work items of one 16-row tile of (sequence, head)
+ *     rows, 16 / G sequences of a group over one 512-token partition of their
+ *     prefix or one sequence's heads over one partition of its suffix; taken when
  *     there is a prefix, the suffix partitions are at most 512 tokens and the
  *     prefix items number at most one per CU;
  *   - otherwise the group's queries (every sequence and head, 128 rows per

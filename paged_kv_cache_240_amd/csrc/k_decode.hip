@@ -40,6 +40,8 @@
 // (single pass) or an fp32 partial plus its base-2 log-sum-exp (split-K),
 // reduced by combine_kernel (Flash Decode's reduce).
 
+#include <algorithm>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -200,6 +202,24 @@ struct StepArgs {
   const float* cos_sin;   // fp32 [max_pos][D]: cos | sin of each position
 };
 
+// Shared-prefix decode in one launch (CASC): grid item x is either 16 / G
+// sequences of a group over prefix partition pp of the group's shared prefix
+// (rows: those sequences times the G heads, one 16-row tile; keys read through
+// the group's first sequence's table; partials in slot slot0 + pp) or one
+// sequence's G heads over partition sp of its tokens after its prefix
+// (partials in slot sp).  Every row sees every key of its item's range.
+struct CascItems {
+  const int32_t* group_start;
+  const int32_t* prefix_lens;
+  int n_pre;       // prefix items: groups * max_sub * pre_parts (first in the grid)
+  int max_sub;     // prefix items per group and partition
+  int pre_parts;   // prefix partitions per group
+  int pre_tokens;  // prefix partition size
+  int suf_parts;   // suffix partitions per sequence
+  int suf_tokens;  // suffix partition size
+  int slot0;       // first prefix slot
+};
+
 // Rotate-half RoPE of 8 consecutive dims j..j+7 of the first half (a) and
 // their partners j+D/2.. (b): lo = a cos - b sin, hi = b cos + a sin, each
 // product and each sum rounded to fp32 on its own (no fused multiply-add),
@@ -249,15 +269,18 @@ __device__ __forceinline__ void substitute_v_rows(uint32_t (&slot)[SLOT], const 
 // FUSED: the decode step's store folded in (see launch_decode_step): q and
 // the new k arrive unrotated, and the new token's K/V row is written to the
 // cache and used from registers.
-template <int D, int G, bool SPLIT, bool ONE, bool FUSED, int WB = kWaveBlocks>
+template <int D, int G, bool SPLIT, bool ONE, bool FUSED, int WB = kWaveBlocks, bool CASC = false>
 __global__ void __launch_bounds__(256, 2)  // 2 waves per SIMD: 8 streaming waves per CU
 decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
               const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
               const int32_t* __restrict__ context_lens, int Hkv, int max_blocks,
               float scale_log2, int part_tokens, int num_parts, uint16_t* __restrict__ out,
               float* __restrict__ o_part, float* __restrict__ lse, const StepArgs st,
-              const int32_t* __restrict__ starts) {
+              const int32_t* __restrict__ starts, const CascItems ci) {
   static_assert(G >= 1 && G <= 8, "query heads per KV head: 1..8");
+  static_assert(!CASC || (SPLIT && ONE && !FUSED), "shared-prefix items are single-chunk partitions");
+  constexpr int NSEQ = CASC ? 16 / G : 1;  // sequences per workgroup
+  constexpr int RM = NSEQ * G;             // rows: (sequence, head) pairs, at most 16
   static_assert(WB == 2 || WB == 4 || WB == 8, "blocks per wave: 2, 4 or 8");
   static_assert(ONE || WB == kWaveBlocks, "a cycling ring takes 8 blocks per wave");
   constexpr int CHUNK_BLOCKS = kWaves * WB;
@@ -271,8 +294,8 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
   constexpr int DEPTH = ONE ? (2 * WB < kDepthOne ? 2 * WB : kDepthOne) : kDepth;
   static_assert(DEPTH % 2 == 0 && (ONE || STEPS % DEPTH == 0), "ring slots must repeat per chunk");
 
-  __shared__ __align__(16) float red[kWaves][G][D];  // per-wave outputs, dim n*DPL+s at s*16+n
-  __shared__ float st_m[kWaves][G], st_l[kWaves][G];
+  __shared__ __align__(16) float red[kWaves][RM][D];  // per-wave outputs, dim n*DPL+s at s*16+n
+  __shared__ float st_m[kWaves][RM], st_l[kWaves][RM];
   // fused step: the new V row's pieces, one copy per wave (lane-major), and
   // the owner wave's new K row, parked between the prologue and their use
   __shared__ uint32_t new_v[FUSED ? kWaves * HALF * 64 : 1];
@@ -283,16 +306,51 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int Hq = Hkv * G;
   const int hq0 = g * G;
-  const int32_t* bt_row = block_tables + (int64_t)b * max_blocks;
-  const int L = context_lens[b];
-  // split-K with starts: sequence b's partitions cover [starts[b], L) (a
-  // shared prefix before it is attended elsewhere); starts[b] is whole blocks
-  const int start = (SPLIT && starts != nullptr) ? starts[b] : 0;
+  // Rows r < R are (sequence seq0 + r / G, head hq0 + r % G); keys through the
+  // table row of sequence b_tab; partials go to slot `slot`.  Without CASC: the
+  // G heads of sequence b, partition p.
+  int R = G, b_tab = b, slot = p, L, start = 0;
+  int64_t seq0 = b;
+  if constexpr (CASC) {
+    int it = p;
+    if (it < ci.n_pre) {
+      const int pp = it % ci.pre_parts;
+      it /= ci.pre_parts;
+      const int gi = it / ci.max_sub, sg = it % ci.max_sub;
+      const int q0 = ci.group_start[gi], q1 = ci.group_start[gi + 1];
+      const int first = q0 + sg * NSEQ;
+      if (first >= q1) return;
+      const int pre = ci.prefix_lens[q0];
+      start = pp * ci.pre_tokens;  // the item's range: [start, min(start + tokens, pre))
+      if (start >= pre) return;
+      L = min(start + ci.pre_tokens, pre);
+      R = min(NSEQ, q1 - first) * G;
+      seq0 = first;
+      b_tab = q0;
+      slot = ci.slot0 + pp;
+    } else {
+      it -= ci.n_pre;
+      const int sp = it % ci.suf_parts, bb = it / ci.suf_parts;
+      const int Lb = context_lens[bb];
+      start = ci.prefix_lens[bb] + sp * ci.suf_tokens;
+      if (start >= Lb) return;  // empty partition: not written, not combined
+      L = min(start + ci.suf_tokens, Lb);
+      seq0 = bb;
+      b_tab = bb;
+      slot = sp;
+    }
+  } else {
+    L = context_lens[b];
+    // split-K with starts: sequence b's partitions cover [starts[b], L) (a
+    // shared prefix before it is attended elsewhere); starts[b] is whole blocks
+    start = (SPLIT && starts != nullptr) ? starts[b] : 0;
+  }
+  const int32_t* bt_row = block_tables + (int64_t)b_tab * max_blocks;
   // The first chunk's table entries are requested before L is known (indices
   // clamped into the table; an entry past the sequence is never dereferenced:
   // it is replaced by the range's first block once L arrives), so the first
   // K/V loads wait for one round trip instead of two.
-  const int lb0 = SPLIT ? (start + p * part_tokens) / kBlockSize : 0;
+  const int lb0 = CASC ? start / kBlockSize : SPLIT ? (start + p * part_tokens) / kBlockSize : 0;
   const int lb_spec = lb0 + wave + kWaves * (threadIdx.x & (WB - 1));
   const int ent_spec = bt_row[min(lb_spec, max_blocks - 1)];
   const int ent_first = bt_row[min(lb0, max_blocks - 1)];  // lb0 may lie past a short suffix
@@ -300,15 +358,20 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
   // B operand of QK: query row of head `col` (zero beyond G), 8 dims per
   // k-step; padding lanes read head 0 and discard it (a select, not a branch)
   uint4 qraw[KS];
+  {
+    const int rr = min(col, R - 1);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qraw[ks] = *reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + hq0 + min(col, G - 1)) * D +
-                                               ks * 32 + quad * 8);
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[ks] = *reinterpret_cast<const uint4*>(q + ((seq0 + rr / G) * Hq + hq0 + rr % G) * D +
+                                                 ks * 32 + quad * 8);
+  }
   // every start-up load is in flight before the emptiness test below
   asm volatile("" ::"v"(ent_spec), "s"(ent_first), "s"(L));
 
   int t_begin = 0, t_end = L;
-  if (SPLIT) {
+  if (CASC) {
+    t_begin = start;
+  } else if (SPLIT) {
     t_begin = start + p * part_tokens;
     if (t_begin >= L) return;  // empty partition: not written, not combined
     t_end = min(t_begin + part_tokens, L);
@@ -434,7 +497,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
       if (owner) rope_rotate8(kraw[ks], kraw[ks + KS / 2], cs_c[ks], cs_s[ks], kr[ks], kr[ks + KS / 2]);
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = col < G ? qr[ks] : make_uint4(0u, 0u, 0u, 0u);
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = col < R ? qr[ks] : make_uint4(0u, 0u, 0u, 0u);
     if (own_wg) {
 #pragma unroll
       for (int w = 0; w < HALF; ++w) new_v[(wave * HALF + w) * 64 + lane] = vraw[w];
@@ -464,7 +527,7 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
     }
   } else {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = col < G ? qraw[ks] : make_uint4(0u, 0u, 0u, 0u);
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = col < R ? qraw[ks] : make_uint4(0u, 0u, 0u, 0u);
   }
 
   for (int c = 0; c < nchunks; ++c) {
@@ -595,14 +658,14 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
   // ---- combine the waves through LDS, write ------------------------------------
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    if (4 * quad + e < G) {
+    if (4 * quad + e < R) {
 #pragma unroll
       for (int s = 0; s < DPL; ++s) red[wave][4 * quad + e][s * 16 + col] = o[s][e];
       if (col == 0) st_l[wave][4 * quad + e] = lacc[e];
     }
-  if (quad == 0 && col < G) st_m[wave][col] = m_run * scale_log2;
+  if (quad == 0 && col < R) st_m[wave][col] = m_run * scale_log2;
   __syncthreads();
-  for (int e = threadIdx.x; e < G * D / 4; e += blockDim.x) {
+  for (int e = threadIdx.x; e < R * D / 4; e += blockDim.x) {
     const int h = e / (D / 4);
     const int d4 = (e % (D / 4)) * 4;  // dims d4..d4+3: lane n = d4 / DPL, tiles s0..s0+3
     const int n = d4 / DPL, s0 = d4 % DPL;
@@ -619,11 +682,11 @@ decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cac
       lsum += wt * st_l[w][h];
     }
     const float inv = 1.f / lsum;
-    const int64_t row = (int64_t)b * Hq + hq0 + h;
+    const int64_t row = (seq0 + h / G) * Hq + hq0 + h % G;
     if (SPLIT) {
-      *reinterpret_cast<float4*>(o_part + (row * num_parts + p) * D + d4) =
+      *reinterpret_cast<float4*>(o_part + (row * num_parts + slot) * D + d4) =
           make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
-      if (d4 == 0) lse[row * num_parts + p] = M + log2f(lsum);
+      if (d4 == 0) lse[row * num_parts + slot] = M + log2f(lsum);
     } else {
       uint2 ov;
       ov.x = pack_bf16x2(sum.x * inv, sum.y * inv);
@@ -682,7 +745,7 @@ hipError_t launch_dg(void* out, float* o_part, float* lse, const void* q, const 
 #define PA_ONE(WBB)                                                                           \
   hipLaunchKernelGGL((decode_kernel<D, G, true, true, FUSED, WBB>), dim3(np, Hkv, B), dim3(256), 0, \
                      stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks, scale_log2,   \
-                     partition_size, np, oo, o_part, lse, st, starts)
+                     partition_size, np, oo, o_part, lse, st, starts, CascItems{})
     if (partition_size <= kChunkTokens) {
       switch (wave_blocks_for(partition_size)) {
         case 2: PA_ONE(2); break;
@@ -692,11 +755,11 @@ hipError_t launch_dg(void* out, float* o_part, float* lse, const void* q, const 
     } else
       hipLaunchKernelGGL((decode_kernel<D, G, true, false, FUSED>), dim3(np, Hkv, B), dim3(256), 0,
                          stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks,
-                         scale_log2, partition_size, np, oo, o_part, lse, st, starts);
+                         scale_log2, partition_size, np, oo, o_part, lse, st, starts, CascItems{});
   } else {
     hipLaunchKernelGGL((decode_kernel<D, G, false, false, FUSED>), dim3(1, Hkv, B), dim3(256), 0,
                        stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks, scale_log2,
-                       0, 1, oo, o_part, lse, st, nullptr);
+                       0, 1, oo, o_part, lse, st, nullptr, CascItems{});
   }
 #undef PA_ONE
   return hipGetLastError();
@@ -762,6 +825,69 @@ hipError_t launch_decode_step(void* out, float* o_part, float* lse, const void* 
   return launch_decode_combine(out, o_part, lse, context_lens, B, Hkv * G, D, np, partition_size, stream);
 }
 
+// Shared-prefix decode in one partition launch (CASC items above).
+hipError_t launch_cascade_decode(float* o_part, float* lse, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, const int32_t* group_start,
+                                 const int32_t* prefix_lens, int B, int num_groups,
+                                 int max_group_size, int max_prefix, int prefix_part,
+                                 int max_suffix, int suffix_part, int slot0, int num_slots,
+                                 int Hq, int Hkv, int D, int max_blocks, float scale,
+                                 hipStream_t stream) {
+  const int G = Hq / Hkv;
+  if (G < 1 || G > 8 || prefix_part <= 0 || prefix_part > kChunkTokens || suffix_part <= 0 ||
+      suffix_part > kChunkTokens)
+    return hipErrorInvalidValue;
+  const int nseq = 16 / G;
+  CascItems ci{};
+  ci.group_start = group_start;
+  ci.prefix_lens = prefix_lens;
+  ci.max_sub = (std::max(max_group_size, 1) + nseq - 1) / nseq;
+  ci.pre_parts = std::max((max_prefix + prefix_part - 1) / prefix_part, 1);
+  ci.pre_tokens = prefix_part;
+  ci.n_pre = (num_groups > 0 && max_prefix > 0) ? num_groups * ci.max_sub * ci.pre_parts : 0;
+  ci.suf_parts = std::max((std::max(max_suffix, 1) + suffix_part - 1) / suffix_part, 1);
+  ci.suf_tokens = suffix_part;
+  ci.slot0 = slot0;
+  const int64_t items = (int64_t)ci.n_pre + (int64_t)B * ci.suf_parts;
+  if (items <= 0) return hipSuccess;
+  if (items > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)items, Hkv, 1);
+  const float sl = scale * 1.4426950408889634f;
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const auto* kc = static_cast<const uint16_t*>(k_cache);
+  const auto* vc = static_cast<const uint16_t*>(v_cache);
+  const StepArgs none{};
+  const int wb = wave_blocks_for(std::max(prefix_part, suffix_part));
+#define PA_CASC1(DD, GG, WBB)                                                                       \
+  hipLaunchKernelGGL((decode_kernel<DD, GG, true, true, false, WBB, true>), grid, dim3(256), 0, stream, \
+                     qq, kc, vc, block_tables, context_lens, Hkv, max_blocks, sl, 0, num_slots,       \
+                     nullptr, o_part, lse, none, nullptr, ci)
+#define PA_CASC(DD, GG)                      \
+  do {                                       \
+    if (wb == 2) PA_CASC1(DD, GG, 2);        \
+    else if (wb == 4) PA_CASC1(DD, GG, 4);   \
+    else PA_CASC1(DD, GG, 8);                \
+  } while (0)
+#define PA_CASC_G(DD)                  \
+  switch (G) {                         \
+    case 1: PA_CASC(DD, 1); break;     \
+    case 2: PA_CASC(DD, 2); break;     \
+    case 3: PA_CASC(DD, 3); break;     \
+    case 4: PA_CASC(DD, 4); break;     \
+    case 5: PA_CASC(DD, 5); break;     \
+    case 6: PA_CASC(DD, 6); break;     \
+    case 7: PA_CASC(DD, 7); break;     \
+    case 8: PA_CASC(DD, 8); break;     \
+    default: return hipErrorInvalidValue; \
+  }
+  if (D == 128) { PA_CASC_G(128) } else { PA_CASC_G(64) }
+#undef PA_CASC_G
+#undef PA_CASC
+#undef PA_CASC1
+  return hipGetLastError();
+}
+
 // Split-K partitions of each sequence's suffix [starts[b], L_b).
 hipError_t launch_decode_suffix(float* o_part, float* lse, const void* q, const void* k_cache,
                                 const void* v_cache, const int32_t* block_tables,
@@ -779,7 +905,7 @@ hipError_t launch_decode_suffix(float* o_part, float* lse, const void* q, const 
 #define PA_SUF1(DD, GG, WBB)                                                                        \
   hipLaunchKernelGGL((decode_kernel<DD, GG, true, true, false, WBB>), dim3(np, Hkv, B), dim3(256), 0, \
                      stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks, scale_log2,    \
-                     partition_size, num_slots, nullptr, o_part, lse, none, starts)
+                     partition_size, num_slots, nullptr, o_part, lse, none, starts, CascItems{})
 #define PA_SUF(DD, GG)                                                                             \
   do {                                                                                             \
     if (partition_size <= kChunkTokens) {                                                          \
@@ -790,7 +916,7 @@ hipError_t launch_decode_suffix(float* o_part, float* lse, const void* q, const 
     } else                                                                                         \
       hipLaunchKernelGGL((decode_kernel<DD, GG, true, false, false>), dim3(np, Hkv, B), dim3(256), 0, \
                          stream, qq, kc, vc, block_tables, context_lens, Hkv, max_blocks,           \
-                         scale_log2, partition_size, num_slots, nullptr, o_part, lse, none, starts); \
+                         scale_log2, partition_size, num_slots, nullptr, o_part, lse, none, starts, CascItems{}); \
   } while (0)
 #define PA_SUF_G(DD)                 \
   switch (G) {                       \

@@ -35,8 +35,6 @@
 // combine kernel over NQ * Hq rows per sequence; a row without a visible key in
 // a partition writes zeros and lse = -inf.
 
-#include <algorithm>
-
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -62,45 +60,23 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Shared-prefix decode in one launch (CASC): work item x of the grid is either
-// a sub-group of `sub` sequences of a group over prefix partition `pp` of the
-// group's shared prefix (rows: the sub-group's sequences times the G heads,
-// keys read through the group's first sequence's table, partials in slot
-// slot0 + pp), or one sequence's G heads over partition `sp` of its tokens
-// after its prefix (partials in slot sp).  Every row sees every key of its
-// item's range.
-struct CascArgs {
-  const int32_t* group_start;
-  const int32_t* prefix_lens;
-  int n_pre;      // prefix items: groups * max_sub * pre_parts (first in the grid)
-  int sub;        // sequences per prefix item
-  int max_sub;    // prefix items per group and partition
-  int pre_parts;  // prefix partitions per group
-  int pre_tokens; // prefix partition size
-  int suf_parts;  // suffix partitions per sequence
-  int suf_tokens; // suffix partition size
-  int slot0;      // first prefix slot
-};
-
 // Ring step s of a chunk (0..15): block pair s / 4; s % 4 = K(2j), K(2j+1), V(2j), V(2j+1).
 __host__ __device__ constexpr int step_block(int s) { return 2 * (s / 4) + (s % 2); }
 __host__ __device__ constexpr bool step_is_v(int s) { return (s % 4) >= 2; }
 
 // ONE: the range is a single chunk (partitions of at most 64 * NW tokens): no
 // refills past it.  NW: waves per workgroup (4, or 8 for single-chunk
-// partitions of up to 1024 tokens, one workgroup per CU).  CASC: the
-// shared-prefix items above (with SPLIT and ONE; q is [B][Hq][D]).
+// partitions of up to 1024 tokens, one workgroup per CU).
 // Two row tiles with a ring that cycles over chunks need more than the 256
 // registers of two waves per SIMD: that variant runs one wave per SIMD.
-template <int D, int G, int CT, bool SPLIT, bool ONE, int NW, bool CASC = false>
+template <int D, int G, int CT, bool SPLIT, bool ONE, int NW>
 __global__ void __launch_bounds__(64 * NW, (CT == 2 && !ONE) || NW == 8 ? 1 : 2)
 decode_multi_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
                     const int32_t* __restrict__ context_lens, int NQ, int Hkv, int max_blocks,
                     float scale_log2, int part_tokens, int num_parts, uint16_t* __restrict__ out,
-                    float* __restrict__ o_part, float* __restrict__ lse, const CascArgs ca) {
+                    float* __restrict__ o_part, float* __restrict__ lse) {
   static_assert(CT == 1 || CT == 2, "one or two 16-row tiles");
-  static_assert(!CASC || (SPLIT && ONE), "shared-prefix items are single-chunk partitions");
   constexpr int kWaves = NW;
   constexpr int kChunk = NW * kWaveBlocks * kBlockSize;  // tokens of one chunk
   constexpr int KS = D / 32;    // QK k-steps over the head dimension
@@ -119,52 +95,12 @@ decode_multi_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int Hq = Hkv * G;
   const int hq0 = g * G;
-  // Rows r < R are (q row seq0 + r / G, head hq0 + r % G); the keys are read
-  // through table row b_tab; partials go to slot `slot` of num_parts.
-  int R, L, b_tab, slot;
-  int64_t seq0;
-  int t_begin = 0, t_end = 0;
-  if constexpr (CASC) {
-    int it = p;
-    if (it < ca.n_pre) {
-      const int pp = it % ca.pre_parts;
-      it /= ca.pre_parts;
-      const int gi = it / ca.max_sub, sg = it % ca.max_sub;
-      const int q0 = ca.group_start[gi], q1 = ca.group_start[gi + 1];
-      const int first = q0 + sg * ca.sub;
-      if (first >= q1) return;
-      const int pre = ca.prefix_lens[q0];
-      t_begin = pp * ca.pre_tokens;
-      if (t_begin >= pre) return;
-      t_end = min(t_begin + ca.pre_tokens, pre);
-      R = min(ca.sub, q1 - first) * G;
-      seq0 = first;
-      b_tab = q0;
-      slot = ca.slot0 + pp;
-    } else {
-      it -= ca.n_pre;
-      const int sp = it % ca.suf_parts, bb = it / ca.suf_parts;
-      const int Lb = context_lens[bb];
-      t_begin = ca.prefix_lens[bb] + sp * ca.suf_tokens;
-      if (t_begin >= Lb) return;  // empty partition: not written, not combined
-      t_end = min(t_begin + ca.suf_tokens, Lb);
-      R = G;
-      seq0 = bb;
-      b_tab = bb;
-      slot = sp;
-    }
-    L = t_end;
-  } else {
-    R = NQ * G;
-    seq0 = (int64_t)b * NQ;
-    b_tab = b;
-    slot = p;
-    L = context_lens[b];
-  }
-  const int32_t* bt_row = block_tables + (int64_t)b_tab * max_blocks;
+  const int R = NQ * G;  // valid rows
+  const int32_t* bt_row = block_tables + (int64_t)b * max_blocks;
+  const int L = context_lens[b];
   // first chunk's table entries requested before L is known (clamped; an entry
   // past the sequence is replaced by the range's first block once L arrives)
-  const int lb0 = CASC ? t_begin / kBlockSize : SPLIT ? p * part_tokens / kBlockSize : 0;
+  const int lb0 = SPLIT ? p * part_tokens / kBlockSize : 0;
   const int lb_spec = lb0 + wave + kWaves * (threadIdx.x & 7);
   const int ent_spec = bt_row[min(lb_spec, max_blocks - 1)];
   const int ent_first = bt_row[lb0];
@@ -177,26 +113,24 @@ decode_multi_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   for (int ct = 0; ct < CT; ++ct) {
     const int r = min(ct * 16 + col, R - 1);  // padding lanes read a valid row, then zero it
     qrow_i[ct] = r / G;
-    const uint16_t* qrow = q + ((seq0 + r / G) * Hq + hq0 + r % G) * D;
+    const uint16_t* qrow = q + (((int64_t)b * NQ + r / G) * Hq + hq0 + r % G) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qraw[ct][ks] = *reinterpret_cast<const uint4*>(qrow + ks * 32 + quad * 8);
   }
   asm volatile("" ::"v"(ent_spec), "s"(ent_first), "s"(L));
 
-  if constexpr (!CASC) {  // (the items set their own range above)
-    t_end = L;
-    if (SPLIT) {
-      t_begin = p * part_tokens;
-      if (t_begin >= L) return;  // empty partition: not written, not combined
-      t_end = min(t_begin + part_tokens, L);
-    } else if (L <= 0) {
-      for (int e = threadIdx.x; e < R * D / 2; e += blockDim.x) {
-        const int r = e / (D / 2);
-        reinterpret_cast<uint32_t*>(out + (((int64_t)b * NQ + r / G) * Hq + hq0 + r % G) * D)[e % (D / 2)] = 0u;
-      }
-      return;
+  int t_begin = 0, t_end = L;
+  if (SPLIT) {
+    t_begin = p * part_tokens;
+    if (t_begin >= L) return;  // empty partition: not written, not combined
+    t_end = min(t_begin + part_tokens, L);
+  } else if (L <= 0) {
+    for (int e = threadIdx.x; e < R * D / 2; e += blockDim.x) {
+      const int r = e / (D / 2);
+      reinterpret_cast<uint32_t*>(out + (((int64_t)b * NQ + r / G) * Hq + hq0 + r % G) * D)[e % (D / 2)] = 0u;
     }
+    return;
   }
 
   uint4 qb[CT][KS];
@@ -204,7 +138,7 @@ decode_multi_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const bool valid = ct * 16 + col < R;
-    lim[ct] = valid ? (CASC ? t_end : min(t_end, L - NQ + qrow_i[ct] + 1)) : t_begin;
+    lim[ct] = valid ? min(t_end, L - NQ + qrow_i[ct] + 1) : t_begin;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qb[ct][ks] = valid ? qraw[ct][ks] : make_uint4(0u, 0u, 0u, 0u);
   }
@@ -408,11 +342,11 @@ decode_multi_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
     // a row without a visible key here contributes nothing: zeros, lse -inf
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const int64_t grow = (seq0 + r / G) * Hq + hq0 + r % G;
+    const int64_t grow = ((int64_t)b * NQ + r / G) * Hq + hq0 + r % G;
     if (SPLIT) {
-      *reinterpret_cast<float4*>(o_part + (grow * num_parts + slot) * D + d4) =
+      *reinterpret_cast<float4*>(o_part + (grow * num_parts + p) * D + d4) =
           make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
-      if (d4 == 0) lse[grow * num_parts + slot] = lsum > 0.f ? M + log2f(lsum) : -INFINITY;
+      if (d4 == 0) lse[grow * num_parts + p] = lsum > 0.f ? M + log2f(lsum) : -INFINITY;
     } else {
       uint2 ov;
       ov.x = pack_bf16x2(sum.x * inv, sum.y * inv);
@@ -435,16 +369,16 @@ hipError_t launch_g(void* out, float* o_part, float* lse, const void* q, const v
     const int np = (mcl + P - 1) / P;
     if (P <= kChunkTokens)
       hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, true, true, 4>), dim3(np, Hkv, B), dim3(256), 0,
-                         stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, P, np, oo, o_part, lse, CascArgs{});
+                         stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, P, np, oo, o_part, lse);
     else if (P <= 2 * kChunkTokens)
       hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, true, true, 8>), dim3(np, Hkv, B), dim3(512), 0,
-                         stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, P, np, oo, o_part, lse, CascArgs{});
+                         stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, P, np, oo, o_part, lse);
     else
       hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, true, false, 4>), dim3(np, Hkv, B), dim3(256), 0,
-                         stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, P, np, oo, o_part, lse, CascArgs{});
+                         stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, P, np, oo, o_part, lse);
   } else {
     hipLaunchKernelGGL((decode_multi_kernel<D, G, CT, false, false, 4>), dim3(1, Hkv, B), dim3(256), 0,
-                       stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, 0, 1, oo, o_part, lse, CascArgs{});
+                       stream, qq, kc, vc, bt, cl, NQ, Hkv, mb, sl, 0, 1, oo, o_part, lse);
   }
   return hipGetLastError();
 }
@@ -472,62 +406,7 @@ hipError_t launch_d(int G, void* out, float* o_part, float* lse, const void* q, 
   return hipErrorInvalidValue;
 }
 
-template <int D>
-hipError_t launch_casc_d(int G, dim3 grid, hipStream_t st, float* o_part, float* lse, const uint16_t* q,
-                         const uint16_t* kc, const uint16_t* vc, const int32_t* bt, const int32_t* cl,
-                         int Hkv, int mb, float sl, int num_slots, const CascArgs& ca) {
-  switch (G) {
-#define PA_CASC_G(GG)                                                                              \
-    case GG:                                                                                       \
-      hipLaunchKernelGGL((decode_multi_kernel<D, GG, 2, true, true, 4, true>), grid, dim3(256), 0, st, \
-                         q, kc, vc, bt, cl, 1, Hkv, mb, sl, 0, num_slots, nullptr, o_part, lse, ca); \
-      return hipGetLastError();
-    PA_CASC_G(1) PA_CASC_G(2) PA_CASC_G(3) PA_CASC_G(4)
-    PA_CASC_G(5) PA_CASC_G(6) PA_CASC_G(7) PA_CASC_G(8)
-#undef PA_CASC_G
-  }
-  return hipErrorInvalidValue;
-}
-
 }  // namespace
-
-hipError_t launch_cascade_partitions(float* o_part, float* lse, const void* q, const void* k_cache,
-                                     const void* v_cache, const int32_t* block_tables,
-                                     const int32_t* context_lens, const int32_t* group_start,
-                                     const int32_t* prefix_lens, int B, int num_groups,
-                                     int max_group_size, int max_prefix, int prefix_part,
-                                     int max_suffix, int suffix_part, int slot0, int num_slots,
-                                     int Hq, int Hkv, int D, int max_blocks, float scale,
-                                     hipStream_t stream) {
-  const int G = Hq / Hkv;
-  if (G < 1 || G > 8 || prefix_part <= 0 || prefix_part > kChunkTokens || suffix_part <= 0 ||
-      suffix_part > kChunkTokens)
-    return hipErrorInvalidValue;
-  CascArgs ca{};
-  ca.group_start = group_start;
-  ca.prefix_lens = prefix_lens;
-  ca.sub = 32 / G;  // sequences per prefix item: up to 32 rows
-  ca.max_sub = (std::max(max_group_size, 1) + ca.sub - 1) / ca.sub;
-  ca.pre_parts = std::max((max_prefix + prefix_part - 1) / prefix_part, 1);
-  ca.pre_tokens = prefix_part;
-  ca.n_pre = (num_groups > 0 && max_prefix > 0) ? num_groups * ca.max_sub * ca.pre_parts : 0;
-  ca.suf_parts = std::max((std::max(max_suffix, 1) + suffix_part - 1) / suffix_part, 1);
-  ca.suf_tokens = suffix_part;
-  ca.slot0 = slot0;
-  const int64_t items = (int64_t)ca.n_pre + (int64_t)B * ca.suf_parts;
-  if (items <= 0) return hipSuccess;
-  if (items > INT32_MAX) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)items, Hkv, 1);
-  const float sl = scale * 1.4426950408889634f;
-  const auto* qq = static_cast<const uint16_t*>(q);
-  const auto* kc = static_cast<const uint16_t*>(k_cache);
-  const auto* vc = static_cast<const uint16_t*>(v_cache);
-  if (D == 128)
-    return launch_casc_d<128>(G, grid, stream, o_part, lse, qq, kc, vc, block_tables, context_lens, Hkv,
-                              max_blocks, sl, num_slots, ca);
-  return launch_casc_d<64>(G, grid, stream, o_part, lse, qq, kc, vc, block_tables, context_lens, Hkv,
-                           max_blocks, sl, num_slots, ca);
-}
 
 hipError_t launch_decode_multi(void* out, float* o_part, float* lse, const void* q,
                                const void* k_cache, const void* v_cache,

@@ -366,14 +366,14 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
   }
   const int32_t suffix_slots = (int32_t)ceil_div(suf, P);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // One partition launch for prefixes and suffixes together: prefix items of up
-  // to 32 rows (32 / G sequences of a group), prefix partitions of kOneLaunchPrefix
+  // One partition launch for prefixes and suffixes together: prefix items of one
+  // 16-row tile (16 / G sequences of a group), prefix partitions of kOneLaunchPrefix
   // tokens; taken when there is a prefix, the suffix partitions are single
   // chunks and the prefix items stay within kOneLaunchMaxItems per CU.  (With no
   // prefix the suffix pass below is pa_decode's own partition kernel.)
   {
     const int32_t Pc = kOneLaunchPrefix;
-    const int64_t sub = 32 / (Hq / Hkv);
+    const int64_t sub = 16 / (Hq / Hkv);
     const int64_t pre_items = (num_groups > 0 && max_prefix > 0)
                                   ? (int64_t)num_groups * ceil_div(std::max(max_group_size, 1), sub) *
                                         ceil_div(max_prefix, Pc) * Hkv
@@ -385,11 +385,10 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
       if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
       float* o_part = static_cast<float*>(workspace);
       float* lse = o_part + (int64_t)B * Hq * slots * D;
-      hipError_t e = pa::launch_cascade_partitions(o_part, lse, q, k_cache, v_cache, block_tables,
-                                                   context_lens, group_start, prefix_lens, B,
-                                                   num_groups, max_group_size, max_prefix, Pc, suf,
-                                                   P, suffix_slots, slots, Hq, Hkv, D, max_blocks,
-                                                   scale, s);
+      hipError_t e = pa::launch_cascade_decode(o_part, lse, q, k_cache, v_cache, block_tables,
+                                               context_lens, group_start, prefix_lens, B, num_groups,
+                                               max_group_size, max_prefix, Pc, suf, P, suffix_slots,
+                                               slots, Hq, Hkv, D, max_blocks, scale, s);
       if (e != hipSuccess) return PA_ERR_HIP;
       return from_hip(pa::launch_decode_combine_cascade(out, o_part, lse, context_lens, prefix_lens,
                                                         B, Hq, D, slots, P, suffix_slots, Pc, s));

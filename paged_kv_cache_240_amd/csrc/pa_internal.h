@@ -95,19 +95,19 @@ hipError_t launch_decode_suffix(float* o_part, float* lse, const void* q, const 
                                 const int32_t* context_lens, const int32_t* starts, int B, int Hq,
                                 int Hkv, int D, int max_blocks, int max_context_len, float scale,
                                 int partition_size, int num_slots, hipStream_t stream);
-// The same decode in one partition launch: items of up to 32 (sequence, head)
-// rows -- a sub-group of a group's sequences over one partition of their shared
-// prefix (slots slot0 + i), or one sequence's heads over a partition of its
-// tokens after the prefix (slots 0..) -- each reading its K/V once.  Partitions
-// of at most 512 tokens; the same reduce follows.
-hipError_t launch_cascade_partitions(float* o_part, float* lse, const void* q, const void* k_cache,
-                                     const void* v_cache, const int32_t* block_tables,
-                                     const int32_t* context_lens, const int32_t* group_start,
-                                     const int32_t* prefix_lens, int B, int num_groups,
-                                     int max_group_size, int max_prefix, int prefix_part,
-                                     int max_suffix, int suffix_part, int slot0, int num_slots,
-                                     int Hq, int Hkv, int D, int max_blocks, float scale,
-                                     hipStream_t stream);
+// The same decode in one partition launch of the decode kernel: items of one
+// 16-row tile -- 16 / G sequences of a group over one partition of their
+// shared prefix (slots slot0 + i), or one sequence's G heads over a partition
+// of its tokens after the prefix (slots 0..) -- each reading its K/V once.
+// Partitions of at most 512 tokens (one chunk); the same reduce follows.
+hipError_t launch_cascade_decode(float* o_part, float* lse, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, const int32_t* group_start,
+                                 const int32_t* prefix_lens, int B, int num_groups,
+                                 int max_group_size, int max_prefix, int prefix_part,
+                                 int max_suffix, int suffix_part, int slot0, int num_slots,
+                                 int Hq, int Hkv, int D, int max_blocks, float scale,
+                                 hipStream_t stream);
 hipError_t launch_decode_combine_cascade(void* out, const float* o_part, const float* lse,
                                          const int32_t* context_lens, const int32_t* starts, int B,
                                          int Hq, int D, int num_slots, int partition_size,

@@ -62,10 +62,10 @@ hipError_t launch_decode_suffix(float*, float*, const void*, const void*, const 
                                 int, int, float, int, int, hipStream_t) {
   return no_device();
 }
-hipError_t launch_cascade_partitions(float*, float*, const void*, const void*, const void*,
-                                     const int32_t*, const int32_t*, const int32_t*, const int32_t*,
-                                     int, int, int, int, int, int, int, int, int, int, int, int, int,
-                                     float, hipStream_t) {
+hipError_t launch_cascade_decode(float*, float*, const void*, const void*, const void*,
+                                 const int32_t*, const int32_t*, const int32_t*, const int32_t*,
+                                 int, int, int, int, int, int, int, int, int, int, int, int, int,
+                                 float, hipStream_t) {
   return no_device();
 }
 hipError_t launch_decode_combine_cascade(void*, const float*, const float*, const int32_t*,

@@ -291,7 +291,7 @@ def test_probe_validation():
     assert lib.pa_probe_gather_read(P, 3 * 4096, P, None) == SHAPE  # tile count not a power of two
     assert lib.pa_probe_gather_read_groups(0) == 0
     assert lib.pa_probe_gather_read_groups(4096) == 1
-    assert lib.pa_probe_gather_read_groups(1 << 31) == (1 << 31) // 4096 // 32
+    assert lib.pa_probe_gather_read_groups(1 << 31) == (1 << 31) // 4096 // 16  # 4 waves x 4 tiles
     assert lib.pa_probe_mfma_bf16(1, None, 1, None) == NULL
     assert lib.pa_probe_mfma_bf16(0, P, 1, None) == SHAPE
     assert lib.pa_probe_mfma_bf16(1, P, 0, None) == SHAPE
