@@ -11,11 +11,11 @@
 // (r = pos * G + h), so the G query heads sharing a KV head share every K/V
 // tile.  A workgroup takes 96 rows and all the keys they can see; its 12 waves
 // form 4 key ranges ("quarters", consecutive runs of 32-key steps) of 3 waves,
-// and each wave owns 32 rows (two 16-row tiles) over its quarter's keys.
-// 96-row workgroups make one workgroup per compute unit on the chunked-prefill
-// shape (32 per (sequence, KV head), 8 pairs); 32 rows per wave keep a wave
-// within 170 registers, so three waves share each SIMD and cover each other's
-// latency, and every K/V operand read from LDS feeds two matrix products.
+// and each wave owns 32 rows (one 32-column tile of the 32x32 products) over
+// its quarter's keys.  96-row workgroups make one workgroup per compute unit
+// on the chunked-prefill shape (32 per (sequence, KV head), 8 pairs); 160
+// registers per wave let three waves share each SIMD and cover each other's
+// latency.
 //
 // Per 32-key step (two 16-token blocks) and quarter:
 //   load  two of the quarter's waves each bring one block's K and V rows straight
@@ -28,22 +28,25 @@
 //         other).  V rows at or past L are fetched from row 0 of their block
 //         (finite data under a zero probability: NaN in unused slots cannot
 //         reach the products).
-//   QK    S^T (keys x rows) = K Q^T on v_mfma_f32_16x16x32_bf16: A = 16 keys
-//         x 32 dims of K from LDS, B = 32 dims x 16 rows of the queries, held
-//         in registers.  A lane ends with 4 consecutive keys of one row.
+//   QK    S^T (32 keys x 32 rows) = K Q^T on v_mfma_f32_32x32x16_bf16, one chain
+//         of D/16 products: A = 32 keys x 16 dims of K from LDS, B = 16 dims x
+//         32 rows of the queries, held in registers.  Lane l ends with 16 keys
+//         (8 (r/4) + 4 (l/32) + r%4) of row l%32.
 //   P     the row's running reference max is raised only when a step's max
 //         exceeds it by more than 2^8 (p then stays below 256: exact enough in
 //         bf16, safe in fp32 sums), which spares nearly every rescale; causal
 //         limits are selects, on steps that cross a row's limit only; p is
-//         rounded to bf16 and the S^T layout is already the B operand of PV.
-//         The row sum accumulates the same rounded p with v_dot2_f32_bf16.
-//   PV    O^T (dims x rows) += V^T P^T: A = 16 dims x 32 keys of V^T, read from
-//         the key-major V tile with the transposing ds_read_b64_tr_b16 (two
-//         reads of 4 keys x 16 dims per operand).
+//         rounded to bf16, and the lane's 16 values are already the B operand
+//         of PV for the key order the V^T reads below use.  The row sum
+//         accumulates the same rounded p with v_dot2_f32_bf16.
+//   PV    O^T (32 dims x 32 rows) += V^T P^T per 32-dim tile and 16-key half:
+//         A = V^T read from the key-major V tile with the transposing
+//         ds_read_b64_tr_b16 (two reads of 4 keys x 16 dims per operand).
 // The quarters meet through LDS at the end (log-sum-exp merge, in two rounds
-// that fit the freed tile buffers).  Workgroup ids are mapped (sequence, KV
-// head)-minor, so consecutive ids -- placed on different XCDs -- take different
-// pairs and each XCD's L2 serves the K/V of few pairs.
+// that fit the freed tile buffers, 16 bytes per lane and access).  Workgroup
+// ids are mapped (sequence, KV head)-minor, so consecutive ids -- placed on
+// different XCDs -- take different pairs and each XCD's L2 serves the K/V of
+// few pairs.
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -56,13 +59,13 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short shortx4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kQuarters = 4;                       // key ranges per workgroup
 constexpr int kWavesPerQ = 3;                      // waves sharing a key range
 constexpr int kWaves = kQuarters * kWavesPerQ;     // 12
 constexpr int kThreads = 64 * kWaves;              // 768
-constexpr int kRowTiles = 2;                       // 16-row tiles per wave
-constexpr int kRowsPerWave = 16 * kRowTiles;       // 32
+constexpr int kRowsPerWave = 32;                   // one 32-column tile per wave
 constexpr int kRowsPerWG = kWavesPerQ * kRowsPerWave;  // 96
 constexpr int kStepKeys = 2 * kBlockSize;          // 32 keys per step
 constexpr float kLazyLog2 = 8.f;                   // reference max may lag by 2^8
@@ -75,17 +78,19 @@ struct Layout {
   static constexpr int BUF = 2 * TILE;             // K tile, then V tile
   static constexpr int KPI = 1024 / ROW;           // key rows per 1 KiB direct load
   static constexpr int IPB = kBlockSize / KPI;     // direct loads per block and tile
-  // XOR swizzles of the 16-byte chunks of a key row, chosen so that each LDS
-  // read below touches distinct banks: in the K tile, chunk c of key k sits in
-  // slot c ^ kx(k); in the V tile, in slot c ^ vx(k).  Both masks leave the
-  // chunk bits that select the operand (k-step of K, dim tile of V) in a field
-  // of their own, so a read's byte address is a per-lane base XOR that field.
+  // XOR swizzles of the 16-byte chunks of a key row: in the K tile, chunk c of
+  // key k sits in slot c ^ kx(k); in the V tile, in slot c ^ vx(k).  kx spreads
+  // the 16 keys a 16-lane group of a K read touches over 16 slots; vx spreads
+  // the 4 keys x 2 chunks of a V^T read's 16-lane group over 8 slots, and keeps
+  // the two groups that read the same keys (the two 16-dim halves of a 32-dim
+  // tile) on disjoint slots.  A read's byte address is a per-lane base XOR the
+  // operand's field (k-step of K, dim tile of V).
   __device__ static __forceinline__ int kx(int k) { return D == 128 ? (k & 15) : ((k >> 1) & 7); }
-  __device__ static __forceinline__ int vx(int k) { return D == 128 ? 2 * (k & 7) : 2 * ((k >> 1) & 3); }
+  __device__ static __forceinline__ int vx(int k) { return D == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
 };
 
-__device__ __forceinline__ floatx4_t mfma16(bf16x8_t a, bf16x8_t b, floatx4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ floatx16_t mfma32(bf16x8_t a, bf16x8_t b, floatx16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
@@ -114,10 +119,10 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                      const int32_t* __restrict__ query_start_loc, int Hkv, int max_blocks, int npairs,
                      float scale_log2) {
   using LY = Layout<D>;
-  constexpr int KS = D / 32;   // QK k-steps over the head dimension
-  constexpr int DT = D / 16;   // 16-dim output tiles
-  constexpr int MERGE = DT * kRowTiles * 4 + 2 * kRowTiles;  // floats per lane of a wave's state
-  static_assert(kWavesPerQ * MERGE * 64 * 4 <= kQuarters * LY::BUF,
+  constexpr int KS = D / 16;   // QK k-steps of 16 dims over the head dimension
+  constexpr int DB = D / 32;   // 32-dim output tiles
+  constexpr int MERGE4 = DB * 4 + 1;  // float4s per lane of a wave's state (O, then m and l)
+  static_assert(kWavesPerQ * MERGE4 * 64 * 16 <= kQuarters * LY::BUF,
                 "one quarter's states fit one set of tile buffers");
 
   // two buffers per quarter, in two arrays (see the header)
@@ -128,7 +133,7 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qq = wave / kWavesPerQ, w = wave % kWavesPerQ;
-  const int col = lane & 15, quad = lane >> 4;
+  const int col = lane & 31, hg = lane >> 5;  // the lane's row in the wave's tile, its key half
   const int pair = blockIdx.x % npairs, rb = blockIdx.x / npairs;
   const int g = pair % Hkv, b = pair / Hkv;
   const int Hq = Hkv * G;
@@ -149,25 +154,19 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   const int64_t head_off = (int64_t)g * kBlockSize * D;
   const int64_t blk_stride = (int64_t)Hkv * kBlockSize * D;
 
-  // ---- this lane's rows (one per 16-row tile: the lane column) -----------------
+  // ---- this lane's row (the lane column of the wave's 32-row tile) ---------------
   const int roww0 = row0 + w * kRowsPerWave;
-  int lim[kRowTiles];
-#pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
-    const int r = roww0 + rt * 16 + col;
-    lim[rt] = L - C + (r < nrows ? r / G : 0);
-  }
-  // B operands of QK: the wave's 32 query rows, 8 dims per k-step (rows past the
-  // chunk read its first row: finite, never written out)
-  bf16x8_t qb[kRowTiles][KS];
-#pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
-    const int r = roww0 + rt * 16 + col;
-    const int rr = r < nrows ? r : row0;
-    const uint16_t* qrow = q + ((int64_t)(q0 + rr / G) * Hq + g * G + rr % G) * D;
+  const int myrow = roww0 + col;
+  const int lim = L - C + (myrow < nrows ? myrow / G : 0);
+  // B operand of QK: the row's query, dims 16 ks + 8 hg .. +7 per k-step (rows
+  // past the chunk read its first row: finite, never written out)
+  bf16x8_t qb[KS];
+  {
+    const int rr = myrow < nrows ? myrow : row0;
+    const uint16_t* qrow = q + ((int64_t)(q0 + rr / G) * Hq + g * G + rr % G) * D + hg * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qb[rt][ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + ks * 32 + quad * 8));
+      qb[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + ks * 16));
   }
   // Steps of this wave's quarter by what its valid rows need: plain (every key
   // visible to every row), crossing some row's limit (selects), or past every
@@ -187,12 +186,13 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   // row of the step, both masks reduce to closed forms in i and j (byte offsets
   // in the block):
   //   K  j*1024 + (kl ^ (j << 6)),      kl = (i / NCH)*ROW + (((i % NCH) ^ (i >> 4)) << 4)
-  //   V  j*1024 + (vl ^ vj),            vl = (i / NCH)*ROW + v0, v0 = ((i % NCH) ^ 2(i >> 4)) << 4
-  //   V, rows at or past L: v0 ^ vj (row 0 of the block), vj = D == 128 ? (j & 1) << 7 : 0.
+  //   V  j*1024 + vl,                   vl = (i / NCH)*ROW + v0,
+  //      v0 = ((i % NCH) ^ vx) << 4 with vx = 4 (i >> 4) (D = 128) or 4 ((i >> 4) & 1) (D = 64)
+  //   V, rows at or past L: v0 (row 0 of the block).
   // Unsigned 32-bit offsets from the block's scalar base keep each load one
   // instruction with a scalar address.
   const uint32_t kl = (uint32_t)((lane / LY::NCH) * LY::ROW + (((lane % LY::NCH) ^ (lane >> 4)) << 4));
-  const uint32_t v0 = (uint32_t)(((lane % LY::NCH) ^ (2 * (lane >> 4))) << 4);
+  const uint32_t v0 = (uint32_t)(((lane % LY::NCH) ^ (D == 128 ? 4 * (lane >> 4) : 4 * ((lane >> 4) & 1))) << 4);
   const uint32_t vl = (uint32_t)((lane / LY::NCH) * LY::ROW) + v0;
   auto entry = [&](int s) { return bt_row[min(s * 2 + min(w, 1), nblk - 1)]; };
   auto issue = [&](int s, int e, unsigned char* dst) {
@@ -203,128 +203,107 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 #pragma unroll
     for (int j = 0; j < LY::IPB; ++j) {
       const int d = (w * kBlockSize + j * LY::KPI) * LY::ROW;
-      const uint32_t vj = D == 128 ? (uint32_t)(j & 1) << 7 : 0u;
       load_lds16(kb + ((uint32_t)j * 1024u + (kl ^ ((uint32_t)j << 6))), dst + d);
       const bool in = tok0 + j * LY::KPI + lane / LY::NCH < L;
-      load_lds16(vb + (in ? (uint32_t)j * 1024u + (vl ^ vj) : (v0 ^ vj)), dst + LY::TILE + d);
+      load_lds16(vb + (in ? (uint32_t)j * 1024u + vl : v0), dst + LY::TILE + d);
     }
   };
 
-  floatx4_t o[DT][kRowTiles];
-  float lsum[kRowTiles], m_ref[kRowTiles];
+  floatx16_t o[DB];  // O^T[dim 32 db + 8 (r / 4) + 4 hg + r % 4][row col] in o[db][r]
+  float lsum = 0.f, m_ref = -INFINITY;
 #pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
-    lsum[rt] = 0.f;
-    m_ref[rt] = -INFINITY;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   const float lazy_raw = kLazyLog2 / scale_log2;
   const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
 
   // Per-lane byte offsets of the operand reads inside a tile.  K (A of QK): key
-  // t*16 + col, chunk ks*4 + quad -> (key*ROW + ((quad ^ kx) bits)) ^ (ks << 6),
-  // the ks field of the chunk being bits 6.. of the offset.  V^T (A of PV, two
-  // transposing reads): lane (l16, quad) reads key 4*quad + l16/4 (+16), dims
-  // 16*dt + 4*(l16 % 4) .. +3 -> (key*ROW + ...) ^ (dt << 5).
-  const int l16 = lane & 15;
-  const int vk = quad * 4 + (l16 >> 2);
-  const int k_lane = col * LY::ROW + (((quad ^ LY::kx(col)) & 3) << 4) + ((LY::kx(col) >> 2) << 6);
-  const int v_lane = vk * LY::ROW + ((((l16 & 3) >> 1) ^ (LY::vx(vk) & 1)) << 4) +
-                     ((LY::vx(vk) >> 1) << 5) + (l16 & 1) * 8;
+  // col, chunk 2 ks + hg -> key*ROW + ((hg ^ kx) << 4), then ^ (ks << 5) per
+  // k-step.  V^T (A of PV, two transposing reads per operand): the lane's
+  // 16-lane group q (dims 16 (q % 2) .. +15 of a 32-dim tile, key half hg)
+  // reads keys 16 h + 4 hg + l16 / 4 (and + 8), dims 4 (l16 % 4) .. +3 of its
+  // 16 -> chunk 2 (q % 2) + (l16 % 4) / 2 of the tile's four, then ^ (db << 6).
+  // The key order this gives the PV contraction (lane half hg, element e:
+  // key 4 hg + e for e < 4, 8 + 4 hg + e - 4 otherwise, + 16 h) is the order
+  // in which the QK result holds the lane's keys, so P needs no exchange.
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int k_lane = col * LY::ROW + ((hg ^ LY::kx(col)) << 4);
+  const int vk = 4 * hg + (l16 >> 2);
+  const int v_lane = vk * LY::ROW + (((2 * (grp & 1) + ((l16 & 3) >> 1)) ^ LY::vx(vk)) << 4) + (l16 & 1) * 8;
 
   // One step from buffer `cur`; `diag`: some key is past some row's limit (the
   // selects are the only code under that branch, so both kinds of step share
   // one body and the accumulators never move between registers).
   auto step = [&](bool diag, int s, const unsigned char* cur) {
     const int z = opaque_zero();  // keeps the read addresses inside the loop
-    const unsigned char* kt = cur + (k_lane + z);
-    const unsigned char* vt = cur + LY::TILE + (v_lane + z);
+    const int kt = k_lane + z;
+    const int vt = v_lane + z;
     const int key0 = s * kStepKeys;
 
-    // ---- QK ---------------------------------------------------------------------
-    floatx4_t st[2][kRowTiles];
+    // ---- QK: S^T (32 keys x 32 rows); lane holds row col, keys 8 (r / 4) + 4 hg + r % 4 ----
+    floatx16_t st;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      bf16x8_t ka[2];
+      const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(cur + (kt ^ (ks << 5)));
+      if (ks == 0) {
+        floatx16_t zero;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        ka[t] = *reinterpret_cast<const bf16x8_t*>(cur + ((kt - cur) ^ (ks << 6)) + t * kBlockSize * LY::ROW);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt)
-          st[t][rt] = mfma16(ka[t], qb[rt][ks], ks == 0 ? floatx4_t{0.f, 0.f, 0.f, 0.f} : st[t][rt]);
+        for (int r = 0; r < 16; ++r) zero[r] = 0.f;
+        st = mfma32(ka, qb[ks], zero);
+      } else {
+        st = mfma32(ka, qb[ks], st);
+      }
     }
     if (diag) {
+      const int d = lim - (key0 + 4 * hg);  // key 8 i + j (+ 4 hg) is visible if 8 i + j <= d
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) {
-          const int d = lim[rt] - (key0 + t * 16 + quad * 4);  // keys j <= d are visible
-#pragma unroll
-          for (int j = 0; j < 4; ++j) st[t][rt][j] = j <= d ? st[t][rt][j] : -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) st[r] = 8 * (r / 4) + (r % 4) <= d ? st[r] : -INFINITY;
     }
     // ---- P ----------------------------------------------------------------------
-    // The lane's own maximum per row decides whether any reference must move;
-    // only then is the row's maximum over its 4 lanes taken (almost never after
-    // the first step: later keys seldom exceed the reference by 2^8).
-    float mt[kRowTiles];
-    bool any = false;
+    // The lane's own maximum decides whether the row's reference must move;
+    // only then is the row's maximum over its two lanes taken.
+    float mt = st[0];
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
-      mt[rt] = maxn(maxn(maxn(st[0][rt][0], st[0][rt][1]), maxn(st[0][rt][2], st[0][rt][3])),
-                    maxn(maxn(st[1][rt][0], st[1][rt][1]), maxn(st[1][rt][2], st[1][rt][3])));
-      any = any || mt[rt] > m_ref[rt] + lazy_raw;  // false for all-masked steps
-    }
+    for (int r = 1; r < 16; ++r) mt = maxn(mt, st[r]);
+    const bool any = mt > m_ref + lazy_raw;  // false for all-masked steps
     if (__builtin_amdgcn_ballot_w64(any)) {
+      mt = maxn_swap32(mt);  // the row's maximum, the same in its 2 lanes
+      const bool raise = mt > m_ref + lazy_raw;
+      const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mt) * scale_log2) : 1.f;
+      m_ref = raise ? mt : m_ref;
+      lsum *= alpha;
 #pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) {
-        mt[rt] = maxn_swap32(maxn_swap16(mt[rt]));  // the row's maximum, the same in its 4 lanes
-        const bool raise = mt[rt] > m_ref[rt] + lazy_raw;
-        const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref[rt] - mt[rt]) * scale_log2) : 1.f;
-        m_ref[rt] = raise ? mt[rt] : m_ref[rt];
-        lsum[rt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
-      }
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
-    bf16x8_t pb[kRowTiles];
+    const float refc = m_ref == -INFINITY ? 0.f : m_ref * scale_log2;
+    uint32_t pk[8];
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
-      const float refc = m_ref[rt] == -INFINITY ? 0.f : m_ref[rt] * scale_log2;
-      uint32_t pk[4];
+    for (int k = 0; k < 8; ++k)
+      pk[k] = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(st[2 * k], scale_log2, -refc)),
+                         __builtin_amdgcn_exp2f(fmaf(st[2 * k + 1], scale_log2, -refc)));
+    float l = lsum;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const floatx4_t& sv = st[t][rt];
-        pk[2 * t] = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[0], scale_log2, -refc)),
-                               __builtin_amdgcn_exp2f(fmaf(sv[1], scale_log2, -refc)));
-        pk[2 * t + 1] = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[2], scale_log2, -refc)),
-                                   __builtin_amdgcn_exp2f(fmaf(sv[3], scale_log2, -refc)));
-      }
-      float l = lsum[rt];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[k]), ones2, l, false);
-      lsum[rt] = l;
-      pb[rt] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    }
+    for (int k = 0; k < 8; ++k)
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[k]), ones2, l, false);
+    lsum = l;
 
-    // ---- PV ---------------------------------------------------------------------
+    // ---- PV: O^T (32 dims x 32 rows) per dim tile, keys in two halves of 16 ----------
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const unsigned char* va1 = cur + LY::TILE + ((vt - cur - LY::TILE) ^ (dt << 5));
-      const shortx4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<shortx4_t>(va1));
-      const shortx4_t a2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          lds_ptr<shortx4_t>(va1 + kBlockSize * LY::ROW));
-      const bf16x8_t va = __builtin_bit_cast(
-          bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(a1, a1, 0, 1)),
-                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(a1, a1, 2, 3)),
-                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(a2, a2, 0, 1)),
-                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(a2, a2, 2, 3))));
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]));
 #pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) o[dt][rt] = mfma16(va, pb[rt], o[dt][rt]);
+      for (int db = 0; db < DB; ++db) {
+        const unsigned char* va1 = cur + LY::TILE + h * kBlockSize * LY::ROW + (vt ^ (db << 6));
+        const shortx4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<shortx4_t>(va1));
+        const shortx4_t a2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<shortx4_t>(va1 + 8 * LY::ROW));
+        const bf16x8_t va = __builtin_bit_cast(
+            bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(a1, a1, 0, 1)),
+                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(a1, a1, 2, 3)),
+                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(a2, a2, 0, 1)),
+                                 __builtin_bit_cast(uint32_t, __builtin_shufflevector(a2, a2, 2, 3))));
+        o[db] = mfma32(va, pb, o[db]);
+      }
     }
   };
 
@@ -362,45 +341,41 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     }
   }
 
-  // ---- row sums over the 4 lanes of each row, then merge the quarters -------------
-#pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
-    float l = lsum[rt];
-    l += swap16(l);
-    lsum[rt] = l + swap32(l);
-  }
-  // a wave's state in merge slot `slot` (0 .. kWavesPerQ-1 in buf_a, the next kWavesPerQ in buf_b): [k][64 lanes]
-  auto at = [&](int slot, int k) -> float& {
-    float* mg = reinterpret_cast<float*>(slot < kWavesPerQ ? &buf_a[0][0] : &buf_b[0][0]);
-    return mg[((slot % kWavesPerQ) * MERGE + k) * 64 + lane];
+  // ---- row sums over the 2 lanes of each row, then merge the quarters -------------
+  lsum += swap32(lsum);
+  // a wave's state in merge slot `slot` (0 .. kWavesPerQ-1 in buf_a, the next
+  // kWavesPerQ in buf_b): [k][64 lanes] of float4
+  auto at = [&](int slot, int k) -> float4& {
+    float4* mg = reinterpret_cast<float4*>(slot < kWavesPerQ ? &buf_a[0][0] : &buf_b[0][0]);
+    return mg[((slot % kWavesPerQ) * MERGE4 + k) * 64 + lane];
   };
   auto put = [&](int slot) {
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) at(slot, (rt * DT + dt) * 4 + j) = o[dt][rt][j];
-      at(slot, DT * kRowTiles * 4 + rt) = m_ref[rt];
-      at(slot, DT * kRowTiles * 4 + kRowTiles + rt) = lsum[rt];
-    }
+      for (int i = 0; i < 4; ++i)
+        at(slot, db * 4 + i) = make_float4(o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]);
+    at(slot, DB * 4) = make_float4(m_ref, lsum, 0.f, 0.f);
   };
   auto take = [&](int slot) {
+    const float4 ml = at(slot, DB * 4);
+    const float m1 = ml.x, l1 = ml.y;
+    const float m0 = m_ref;
+    const float M = fmaxf(m0, m1);
+    const float w0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m0 - M) * scale_log2);
+    const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - M) * scale_log2);
+    m_ref = M;
+    lsum = w0 * lsum + w1 * l1;
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
-      const float m1 = at(slot, DT * kRowTiles * 4 + rt);
-      const float l1 = at(slot, DT * kRowTiles * 4 + kRowTiles + rt);
-      const float m0 = m_ref[rt];
-      const float M = fmaxf(m0, m1);
-      const float w0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m0 - M) * scale_log2);
-      const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - M) * scale_log2);
-      m_ref[rt] = M;
-      lsum[rt] = w0 * lsum[rt] + w1 * l1;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[dt][rt][j] = w0 * o[dt][rt][j] + w1 * at(slot, (rt * DT + dt) * 4 + j);
-    }
+      for (int i = 0; i < 4; ++i) {
+        const float4 v = at(slot, db * 4 + i);
+        o[db][4 * i] = w0 * o[db][4 * i] + w1 * v.x;
+        o[db][4 * i + 1] = w0 * o[db][4 * i + 1] + w1 * v.y;
+        o[db][4 * i + 2] = w0 * o[db][4 * i + 2] + w1 * v.z;
+        o[db][4 * i + 3] = w0 * o[db][4 * i + 3] + w1 * v.w;
+      }
   };
   // round 1: quarters 2, 3 hand over to quarters 0, 1; round 2: quarter 1 to quarter 0
   if (qq >= 2) put((qq - 2) * kWavesPerQ + w);
@@ -413,19 +388,19 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   take(w);
 
   // ---- normalise and write ------------------------------------------------------------
+  if (myrow >= nrows) return;
+  {
+    const int pos = myrow / G, h = myrow % G;
+    const float inv = 1.f / lsum;
+    uint16_t* orow = out + ((int64_t)(q0 + pos) * Hq + g * G + h) * D + 4 * hg;
 #pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
-    const int r = roww0 + rt * 16 + col;
-    if (r >= nrows) continue;
-    const int pos = r / G, h = r % G;
-    const float inv = 1.f / lsum[rt];
-    uint16_t* orow = out + ((int64_t)(q0 + pos) * Hq + g * G + h) * D;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const floatx4_t y = o[dt][rt] * inv;
-      *reinterpret_cast<uint2*>(orow + dt * 16 + quad * 4) =
-          make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-    }
+      for (int i = 0; i < 4; ++i) {
+        const float y0 = o[db][4 * i] * inv, y1 = o[db][4 * i + 1] * inv;
+        const float y2 = o[db][4 * i + 2] * inv, y3 = o[db][4 * i + 3] * inv;
+        *reinterpret_cast<uint2*>(orow + db * 32 + 8 * i) = make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+      }
   }
 }
 
