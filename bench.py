@@ -28,6 +28,7 @@ committed files only):
     python bench.py --mode verify-kernel  # 3 x 28 calls of pa_decode_multi (5 queries per sequence)
     python bench.py --mode cb-cold  # continuous-batching step, 10 cold calls of each path
     python bench.py --mode copy-calibration  # torch copy of 1 GiB (FETCH/WRITE_SIZE scale)
+    python bench.py --mode issue-probe  # matrix products beside exp2/FMA chains, 1-3 waves per SIMD
     python bench.py --mode write-traffic --pmc F_STEP W_STEP F_COPY W_COPY
         # profiles/decode_partitions_traffic.json from the four counter folders
 """
@@ -775,7 +776,8 @@ def main():
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--mode", default="bench",
                     choices=["bench", "decode-kernel", "partition-kernel", "prefill-kernel",
-                             "verify-kernel", "cb-cold", "copy-calibration", "write-traffic"])
+                             "verify-kernel", "cb-cold", "copy-calibration", "write-traffic",
+                             "issue-probe"])
     ap.add_argument("--pmc", nargs=4, metavar=("FETCH_STEP", "WRITE_STEP", "FETCH_COPY", "WRITE_COPY"),
                     help="write-traffic: the four rocprofv3 --pmc output folders")
     args = ap.parse_args()
@@ -796,6 +798,26 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.mode == "issue-probe":
+        # pa_probe_issue_mix: per launch, each wave runs 4096 iterations of 16 products
+        # (mode 1), 32 exp2 + FMA steps per lane (mode 2) or both (mode 3); one to three
+        # waves per SIMD (grid = CUs x waves); SIMD cycles per iteration at the nominal
+        # 2.4 GHz clock
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        iters = 4096
+        table = []
+        for wps in (1, 2, 3):
+            row = {"waves_per_simd": wps}
+            for mode, name in ((1, "products"), (2, "exp2_fma"), (3, "both")):
+                call = probes.prepare_probe_issue_mix(mode, iters, cus * wps, dev)
+                us = time_calls(call, 5, warm=2)
+                row[name + "_us"] = round(us, 2)
+                row[name + "_cycles_per_iter"] = round(us * 1e-6 * 2.4e9 / iters)
+            row["overlap_saved_frac"] = round(1 - row["both_us"] / (row["products_us"] + row["exp2_fma_us"]), 3)
+            table.append(row)
+            print(json.dumps(row), flush=True)
+        print(json.dumps({"mode": "issue-probe", "iters": iters, "cus": cus, "rows": table}))
+        return
     if args.mode == "copy-calibration":
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -107,7 +107,55 @@ mfma_bf16_kernel(int iters, float* __restrict__ out) {
     out[blockIdx.x * (kProbeThreads / 64) + (threadIdx.x >> 6)] = c0[0] + c1[0] + c2[0] + c3[0];
 }
 
+// Issue mix: per iteration, a wave runs (mode & 1) sixteen 16x16x32 bf16
+// products on bf16 ones into 8 independent accumulators, and/or (mode & 2)
+// thirty-two exp2 + FMA steps on 16 independent chains.  Each lane writes
+// out[thread] = (sum of its accumulators' first elements) + (sum of its
+// chains), both deterministic; timing the launch per mode and per waves per
+// SIMD shows whether the SIMD overlaps the two kinds of work.
+template <int MODE>
+__global__ void __launch_bounds__(kProbeThreads)
+issue_mix_kernel(int iters, float* __restrict__ out) {
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
+                                                                0x3F803F80u, 0x3F803F80u));
+  floatx4_t c[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) c[k] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float v[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] = 1e-3f * (float)((threadIdx.x & 63) + k);
+  for (int it = 0; it < iters; ++it) {
+    if constexpr ((MODE & 1) != 0) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ones, c[k], 0, 0, 0);
+    }
+    if constexpr ((MODE & 2) != 0) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = __builtin_amdgcn_exp2f(fmaf(v[k], -0.5f, 0.125f));  // contracts to a fixed point
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sum += c[k][0];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) sum += v[k];
+  out[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = sum;
+}
+
 }  // namespace
+
+hipError_t launch_probe_issue_mix(int mode, int iters, float* out, int grid, hipStream_t stream) {
+  switch (mode) {
+    case 1: hipLaunchKernelGGL(issue_mix_kernel<1>, dim3(grid), dim3(kProbeThreads), 0, stream, iters, out); break;
+    case 2: hipLaunchKernelGGL(issue_mix_kernel<2>, dim3(grid), dim3(kProbeThreads), 0, stream, iters, out); break;
+    default: hipLaunchKernelGGL(issue_mix_kernel<3>, dim3(grid), dim3(kProbeThreads), 0, stream, iters, out); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sums, int grid,
                                     hipStream_t stream) {

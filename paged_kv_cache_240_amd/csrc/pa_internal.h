@@ -73,6 +73,7 @@ hipError_t launch_prefill(void* out, const void* q, const void* k_cache, const v
 hipError_t launch_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sums, int grid,
                                     hipStream_t stream);
 hipError_t launch_probe_mfma_bf16(int iters, float* out, int grid, hipStream_t stream);
+hipError_t launch_probe_issue_mix(int mode, int iters, float* out, int grid, hipStream_t stream);
 // A one-pass gather of `bytes` (a power-of-two count of 4 KiB tiles) in
 // scrambled 4 KiB tiles, one 32-bit sum per workgroup to
 // sums[probe_gather_read_groups(bytes)].

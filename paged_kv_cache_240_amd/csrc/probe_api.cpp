@@ -38,4 +38,10 @@ pa_status pa_probe_mfma_bf16(int32_t iters, float* out, int32_t grid, pa_stream_
   return from_hip(pa::launch_probe_mfma_bf16(iters, out, grid, static_cast<hipStream_t>(stream)));
 }
 
+pa_status pa_probe_issue_mix(int32_t mode, int32_t iters, float* out, int32_t grid, pa_stream_t stream) {
+  if (!out) return PA_ERR_NULL;
+  if (mode < 1 || mode > 3 || iters <= 0 || grid <= 0) return PA_ERR_SHAPE;
+  return from_hip(pa::launch_probe_issue_mix(mode, iters, out, grid, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

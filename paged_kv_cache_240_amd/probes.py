@@ -1,6 +1,7 @@
 """ctypes binding of libpa_probe.so, the device-ceiling measurement kernels
 (include/pa_probe.h): a streaming read, a scrambled 4 KiB-tile gather and bf16
-matrix-core chains.  Used by the benchmark to report what the device reaches
+matrix-core chains, and an issue-mix probe (matrix products beside exp2/FMA
+chains).  Used by the benchmark to report what the device reaches
 beside its published figures; not part of the paged-attention ABI."""
 
 import ctypes
@@ -20,6 +21,7 @@ _SIGS = {
     "pa_probe_mfma_bf16": (ctypes.c_int, [_i32, _p, _i32, _p]),
     "pa_probe_gather_read_groups": (ctypes.c_int64, [_i64]),
     "pa_probe_gather_read": (ctypes.c_int, [_p, _i64, _p, _p]),
+    "pa_probe_issue_mix": (ctypes.c_int, [_i32, _i32, _p, _i32, _p]),
 }
 _lib = None
 
@@ -82,4 +84,13 @@ def prepare_probe_mfma_bf16(iters, grid, device, out=None):
     if out is None:
         out = torch.empty(4 * grid, dtype=torch.float32, device=device)
     return ProbeCall("pa_probe_mfma_bf16", (int(iters), _ptr(out), int(grid), _stream(out.device)),
+                     result=out)
+
+
+def prepare_probe_issue_mix(mode, iters, grid, device, out=None):
+    """pa_probe_issue_mix: mode 1 (products), 2 (exp2 + FMA chains) or 3 (both);
+    returns a callable whose result is the fp32 [256 * grid] per-thread values."""
+    if out is None:
+        out = torch.empty(256 * grid, dtype=torch.float32, device=device)
+    return ProbeCall("pa_probe_issue_mix", (int(mode), int(iters), _ptr(out), int(grid), _stream(out.device)),
                      result=out)

@@ -295,6 +295,11 @@ def test_probe_validation():
     assert lib.pa_probe_mfma_bf16(1, None, 1, None) == NULL
     assert lib.pa_probe_mfma_bf16(0, P, 1, None) == SHAPE
     assert lib.pa_probe_mfma_bf16(1, P, 0, None) == SHAPE
+    assert lib.pa_probe_issue_mix(1, 1, None, 1, None) == NULL
+    assert lib.pa_probe_issue_mix(0, 1, P, 1, None) == SHAPE
+    assert lib.pa_probe_issue_mix(4, 1, P, 1, None) == SHAPE
+    assert lib.pa_probe_issue_mix(3, 0, P, 1, None) == SHAPE
+    assert lib.pa_probe_issue_mix(3, 1, P, 0, None) == SHAPE
 
 
 def _sp(**kw):
