@@ -69,6 +69,19 @@ def test_several_groups(gpu, D, G):
     _run(gpu, b, groups, [16, 64, 512, 1024, -1], f"G={G} D={D}")  # 1024: the three-launch path
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 3, 5, 7])
+def test_group_split_over_items(gpu, D, G):
+    # a group of 13 sequences: the one-launch form splits it into items of 16 // G
+    # sequences (a partial last item unless 16 // G divides 13; rows past 16 // G * G
+    # padding), over a 576-token prefix (a partial 512-token prefix partition)
+    lens = [576 + 16 + 37 * i for i in range(13)] + [300, 45]
+    Hkv = 2 if G <= 4 else 1
+    b = W.decode_batch(lens, G * Hkv, Hkv, D, 1024, 6300 + 10 * G + D, theta=1e4, poison=True,
+                       table_fill=W.INT32_MIN)
+    _run(gpu, b, [(0, 13, 576)], [64, 512, -1], f"13-sequence group G={G} D={D}")
+
+
 def test_without_groups_equals_decode(gpu):
     # every prefix 0: the same partitions and reduce as pa_decode, bit for bit
     b = W.decode_batch([1, 17, 500, 1000, 33], 12, 2, 128, 256, 6201, theta=1e4)
