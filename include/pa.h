@@ -301,10 +301,11 @@ pa_status pa_decode_step_partitions(float* o_part, float* lse, const void* q, co
  *     prefix or one sequence's heads over one partition of its suffix; taken when
  *     there is a prefix, the suffix partitions are at most 512 tokens and the
  *     prefix items number at most one per CU;
- *   - otherwise the group's queries (every sequence and head, 128 rows per
- *     workgroup) attend each partition of the prefix (128 to 1024 tokens)
- *     together on the matrix cores, then the suffix partitions, then the reduce.
- * It pays when many sequences share a long prefix (measured: 2.0x pa_decode
+ *   - otherwise the group's queries (every sequence and head, 96 rows per
+ *     workgroup) attend each partition of the prefix (512 tokens, 128 to 1024
+ *     when the grid or the workspace slots need it) together on the matrix
+ *     cores, then the suffix partitions, then the reduce.
+ * It pays when many sequences share a long prefix (measured: 2.1x pa_decode
  * for 128 sequences sharing 4096 tokens); for a few sequences on a prefix that
  * stays in the last-level cache, pa_decode is faster.
  *

@@ -27,7 +27,7 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 PER_FILE = {"k_cache_store.hip": ["-ffp-contract=off"]}
-SOURCES = ["pa_api.cpp", "k_cache_store.hip", "k_decode.hip", "k_decode_multi.hip", "k_prefill.hip", "k_prefill_chunk.hip", "k_blocks.hip",
+SOURCES = ["pa_api.cpp", "k_cache_store.hip", "k_decode.hip", "k_decode_multi.hip", "k_prefill_chunk.hip", "k_blocks.hip",
            "k_norm_act.hip", "block_manager.cpp", "pa_noalloc.hip"]
 PROBE_SOURCES = ["probe_api.cpp", "k_probe.hip"]
 

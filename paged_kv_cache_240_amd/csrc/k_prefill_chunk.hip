@@ -111,13 +111,34 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, lds_ptr<void>(lds), 16, 0, 0);
 }
 
-template <int D, int G>
+// Shared-prefix mode (PART): the decode queries of a group of sequences that
+// share their first blocks attend one partition of that prefix together.
+// Group gi is sequences group_start[gi] .. group_start[gi+1]-1, all with the
+// same first prefix_lens[group_start[gi]] tokens (whole blocks, read through
+// the first sequence's table).  Work item (gi, kp, KV head g) takes rows
+// (sequence s of the group, head h) r = s*G + h -- the decode queries are
+// q[B][Hq][D], so sequence s of the group is "position" s -- and keys
+// [kp*part_tokens, min((kp+1)*part_tokens, prefix)) with no causal mask, and
+// writes the normalised fp32 partial and its base-2 log-sum-exp to slot
+// slot0 + kp of each row, in the split-K workspace layout.
+struct GroupArgs {
+  const int32_t* group_start;
+  const int32_t* prefix_lens;
+  int part_tokens;  // multiple of 32
+  int parts;        // partitions per group
+  int slot0;        // first workspace slot of the prefix partitions
+  int num_slots;    // slots per row in the workspace
+  float* o_part;    // [B][Hq][num_slots][D]
+  float* lse;       // [B][Hq][num_slots]
+};
+
+template <int D, int G, bool PART = false>
 __global__ void __launch_bounds__(kThreads, 1)
 chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                      const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
                      const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
                      const int32_t* __restrict__ query_start_loc, int Hkv, int max_blocks, int npairs,
-                     float scale_log2) {
+                     float scale_log2, const GroupArgs ga) {
   using LY = Layout<D>;
   constexpr int KS = D / 16;   // QK k-steps of 16 dims over the head dimension
   constexpr int DB = D / 32;   // 32-dim output tiles
@@ -138,26 +159,42 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   const int g = pair % Hkv, b = pair / Hkv;
   const int Hq = Hkv * G;
 
-  const int q0 = query_start_loc[b];
-  const int C = query_start_loc[b + 1] - q0;
-  const int L = context_lens[b];
+  // Chunked prefill: rows of sequence b's chunk, keys [0, kmax) under the causal
+  // limits.  PART: rows of group gi, keys [kbeg, L) with L the partition's end.
+  int q0, C, L, kbeg = 0, kp = 0, seq_tab = b;
+  if constexpr (PART) {
+    const int gi = b / ga.parts;
+    kp = b % ga.parts;
+    q0 = ga.group_start[gi];
+    C = ga.group_start[gi + 1] - q0;  // sequences of the group
+    const int pre = ga.prefix_lens[q0];
+    kbeg = kp * ga.part_tokens;
+    if (kbeg >= pre) return;
+    L = min(kbeg + ga.part_tokens, pre);
+    seq_tab = q0;
+  } else {
+    q0 = query_start_loc[b];
+    C = query_start_loc[b + 1] - q0;
+    L = context_lens[b];
+  }
   const int nrows = C * G;
   const int row0 = rb * kRowsPerWG;
   if (row0 >= nrows) return;  // the whole workgroup leaves together
   const int last_row = min(nrows, row0 + kRowsPerWG) - 1;
-  const int kmax = L - C + last_row / G + 1;          // keys any row of the workgroup sees
-  const int ns = (kmax + kStepKeys - 1) / kStepKeys;  // steps of the workgroup
-  const int s_begin = qq * ns / kQuarters, s_end = (qq + 1) * ns / kQuarters;
+  const int kmax = PART ? L : L - C + last_row / G + 1;  // keys any row of the workgroup sees
+  const int sbase = kbeg / kStepKeys;
+  const int ns = (kmax - kbeg + kStepKeys - 1) / kStepKeys;  // steps of the workgroup
+  const int s_begin = sbase + qq * ns / kQuarters, s_end = sbase + (qq + 1) * ns / kQuarters;
   const int niter = (ns + kQuarters - 1) / kQuarters;  // steps of the largest quarter
   const int nblk = (L + kBlockSize - 1) / kBlockSize;
-  const int32_t* bt_row = block_tables + (int64_t)b * max_blocks;
+  const int32_t* bt_row = block_tables + (int64_t)seq_tab * max_blocks;
   const int64_t head_off = (int64_t)g * kBlockSize * D;
   const int64_t blk_stride = (int64_t)Hkv * kBlockSize * D;
 
   // ---- this lane's row (the lane column of the wave's 32-row tile) ---------------
   const int roww0 = row0 + w * kRowsPerWave;
   const int myrow = roww0 + col;
-  const int lim = L - C + (myrow < nrows ? myrow / G : 0);
+  const int lim = PART ? L - 1 : L - C + (myrow < nrows ? myrow / G : 0);
   // B operand of QK: the row's query, dims 16 ks + 8 hg .. +7 per k-step (rows
   // past the chunk read its first row: finite, never written out)
   bf16x8_t qb[KS];
@@ -173,8 +210,8 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   // row's limit (not computed).
   int plain_end = s_begin, comp_end = s_begin;
   if (roww0 < nrows) {
-    const int lim_lo = L - C + roww0 / G;
-    const int lim_hi = L - C + min(nrows - 1, roww0 + kRowsPerWave - 1) / G;
+    const int lim_lo = PART ? L - 1 : L - C + roww0 / G;
+    const int lim_hi = PART ? L - 1 : L - C + min(nrows - 1, roww0 + kRowsPerWave - 1) / G;
     plain_end = min(max((lim_lo + 1) / kStepKeys, s_begin), s_end);
     comp_end = min(max(lim_hi / kStepKeys + 1, s_begin), s_end);
   }
@@ -389,7 +426,20 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 
   // ---- normalise and write ------------------------------------------------------------
   if (myrow >= nrows) return;
-  {
+  if constexpr (PART) {
+    // partial of row (sequence q0 + pos, head g*G + h) at slot slot0 + kp
+    const int pos = myrow / G, h = myrow % G;
+    const float inv = 1.f / lsum;
+    const int64_t slot = ((int64_t)(q0 + pos) * Hq + g * G + h) * ga.num_slots + ga.slot0 + kp;
+    float* orow = ga.o_part + slot * D + 4 * hg;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4*>(orow + db * 32 + 8 * i) =
+            make_float4(o[db][4 * i] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
+    if (hg == 0) ga.lse[slot] = m_ref * scale_log2 + log2f(lsum);
+  } else {
     const int pos = myrow / G, h = myrow % G;
     const float inv = 1.f / lsum;
     uint16_t* orow = out + ((int64_t)(q0 + pos) * Hq + g * G + h) * D + 4 * hg;
@@ -404,13 +454,14 @@ chunk_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   }
 }
 
-template <int D>
+template <int D, bool PART = false>
 hipError_t launch_chunk_d(int G, dim3 grid, hipStream_t stream, uint16_t* out, const uint16_t* q,
                           const uint16_t* kc, const uint16_t* vc, const int32_t* bt, const int32_t* cl,
-                          const int32_t* qsl, int Hkv, int mb, int npairs, float sl) {
-#define PA_CHUNK(GG)                                                                              \
-  hipLaunchKernelGGL((chunk_prefill_kernel<D, GG>), grid, dim3(kThreads), 0, stream, out, q, kc, vc, \
-                     bt, cl, qsl, Hkv, mb, npairs, sl)
+                          const int32_t* qsl, int Hkv, int mb, int npairs, float sl,
+                          const GroupArgs& ga = GroupArgs{}) {
+#define PA_CHUNK(GG)                                                                                     \
+  hipLaunchKernelGGL((chunk_prefill_kernel<D, GG, PART>), grid, dim3(kThreads), 0, stream, out, q, kc, vc, \
+                     bt, cl, qsl, Hkv, mb, npairs, sl, ga)
   switch (G) {
     case 1: PA_CHUNK(1); break;
     case 2: PA_CHUNK(2); break;
@@ -449,6 +500,38 @@ hipError_t launch_prefill(void* out, const void* q, const void* k_cache, const v
                                query_start_loc, Hkv, max_blocks, Hkv * B, sl);
   return launch_chunk_d<64>(G, grid, stream, o, qq, kc, vc, block_tables, context_lens,
                             query_start_loc, Hkv, max_blocks, Hkv * B, sl);
+}
+
+int64_t group_prefix_row_blocks(int max_group_size, int G) {
+  return ((int64_t)max_group_size * G + kRowsPerWG - 1) / kRowsPerWG;
+}
+
+// Shared-prefix partials of decode queries on the chunked-prefill kernel: work
+// items (groups * parts * Hkv) x row blocks.
+hipError_t launch_group_prefix(float* o_part, float* lse, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* group_start, const int32_t* prefix_lens, int groups,
+                               int max_group_size, int max_prefix, int part_tokens, int slot0,
+                               int num_slots, int Hq, int Hkv, int D, int max_blocks, float scale,
+                               hipStream_t stream) {
+  const int G = Hq / Hkv;
+  if (part_tokens <= 0 || part_tokens % kStepKeys != 0) return hipErrorInvalidValue;
+  const int parts = (max_prefix + part_tokens - 1) / part_tokens;
+  const int64_t rblocks = group_prefix_row_blocks(max_group_size, G);
+  const int64_t npairs = (int64_t)groups * parts * Hkv;
+  if (groups <= 0 || parts <= 0 || rblocks <= 0) return hipSuccess;
+  if (npairs * rblocks > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(npairs * rblocks));
+  const GroupArgs ga{group_start, prefix_lens, part_tokens, parts, slot0, num_slots, o_part, lse};
+  const float sl = scale * 1.4426950408889634f;
+  auto* qq = static_cast<const uint16_t*>(q);
+  auto* kc = static_cast<const uint16_t*>(k_cache);
+  auto* vc = static_cast<const uint16_t*>(v_cache);
+  if (D == 128)
+    return launch_chunk_d<128, true>(G, grid, stream, nullptr, qq, kc, vc, block_tables, nullptr,
+                                     nullptr, Hkv, max_blocks, (int)npairs, sl, ga);
+  return launch_chunk_d<64, true>(G, grid, stream, nullptr, qq, kc, vc, block_tables, nullptr, nullptr,
+                                  Hkv, max_blocks, (int)npairs, sl, ga);
 }
 
 }  // namespace pa

@@ -292,7 +292,7 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
 }
 
 namespace {
-constexpr int kPrefixPartTokens = 128;  // smallest shared-prefix partition: a key tile per half
+constexpr int kPrefixPartTokens = 128;  // smallest shared-prefix partition: one 32-key step per key range
 constexpr int kMaxCascadeSlots = 64;
 constexpr int kOneLaunchPrefix = 512;   // prefix partition of the one-launch path
 constexpr int kOneLaunchMaxItems = 1;   // its prefix items per CU, at most
@@ -301,24 +301,21 @@ int32_t cascade_slots(int32_t max_suffix, int32_t P, int32_t max_prefix, int32_t
   return (int32_t)(ceil_div(max_suffix, P) + ceil_div(max_prefix, Pg));
 }
 
-// Prefix partition size: each group workgroup costs a fixed latency (about 8
-// us: its loads, one LDS stage, the merge of its halves) plus about 3 us per
-// 128 keys, and workgroups beyond one per CU run in further rounds; take the
-// size with the least estimated time whose slots fit.
+// Prefix partition size of the group pass: 512 tokens (measured best or
+// within a few percent of the best on groups of 64-256 sequences over
+// 2000-8192-token prefixes: smaller partitions multiply the partials to write
+// and reduce, larger ones leave CUs idle); halved while the grid would hold
+// fewer workgroups than a quarter of the CUs, doubled while the slots would
+// not fit; 0 if no size fits.
 int32_t prefix_partition(int32_t row_blocks, int32_t max_prefix, int32_t suffix_slots) {
   const int cus = device_cu_count();
-  int32_t best = 0;
-  double best_t = 1e30;
-  for (int32_t Pg = kPrefixPartTokens; Pg <= 8 * kPrefixPartTokens; Pg *= 2) {
-    if (suffix_slots + ceil_div(max_prefix, Pg) > kMaxCascadeSlots) continue;
-    const int64_t wgs = (int64_t)row_blocks * ceil_div(max_prefix, Pg);
-    const double t = (double)ceil_div(wgs, cus) * (8.0 + 3.0 * Pg / kPrefixPartTokens);
-    if (t < best_t) {
-      best_t = t;
-      best = Pg;
-    }
+  int32_t Pg = 4 * kPrefixPartTokens;
+  while (Pg > kPrefixPartTokens && (int64_t)row_blocks * ceil_div(max_prefix, Pg) < cus / 4) Pg /= 2;
+  while (suffix_slots + ceil_div(max_prefix, Pg) > kMaxCascadeSlots) {
+    if (Pg >= 8 * kPrefixPartTokens) return 0;
+    Pg *= 2;
   }
-  return best;
+  return Pg;
 }
 }  // namespace
 
@@ -394,10 +391,10 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
                                                         B, Hq, D, slots, P, suffix_slots, Pc, s));
     }
   }
-  // Otherwise the group pass on the matrix cores (128-row workgroups), then the
-  // suffix partitions, then the reduce.
-  // row blocks of 128 (sequence, head) rows per group, times KV heads and groups
-  const int32_t row_blocks = (int32_t)(ceil_div((int64_t)std::max(max_group_size, 1) * (Hq / Hkv), 128) *
+  // Otherwise the group pass on the matrix cores (the chunked-prefill kernel's
+  // 96-row workgroups), then the suffix partitions, then the reduce.
+  // row blocks of (sequence, head) rows per group, times KV heads and groups
+  const int32_t row_blocks = (int32_t)(pa::group_prefix_row_blocks(std::max(max_group_size, 1), Hq / Hkv) *
                                        Hkv * std::max(num_groups, 1));
   const int32_t Pg = max_prefix > 0 ? prefix_partition(row_blocks, max_prefix, suffix_slots)
                                     : kPrefixPartTokens;

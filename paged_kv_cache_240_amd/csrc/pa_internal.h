@@ -81,10 +81,13 @@ int64_t probe_gather_read_groups(int64_t bytes);
 hipError_t launch_probe_gather_read(const void* buf, int64_t bytes, uint32_t* sums,
                                     hipStream_t stream);
 
-// Shared-prefix decode: the group prefixes' partials (prefill kernel, group
-// mode), the suffix partitions of each sequence from starts[b], and their
-// log-sum-exp reduce.  Workspace rows hold num_slots partials: suffix
-// partitions from slot 0, prefix partitions from slot0.
+// Shared-prefix decode: the group prefixes' partials (chunked-prefill kernel,
+// group mode: rows of up to group_prefix_row_blocks(max_group_size, G) row
+// blocks per (group, partition, KV head); part_tokens a multiple of 32), the
+// suffix partitions of each sequence from starts[b], and their log-sum-exp
+// reduce.  Workspace rows hold num_slots partials: suffix partitions from slot
+// 0, prefix partitions from slot0.
+int64_t group_prefix_row_blocks(int max_group_size, int G);
 hipError_t launch_group_prefix(float* o_part, float* lse, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_tables,
                                const int32_t* group_start, const int32_t* prefix_lens, int groups,

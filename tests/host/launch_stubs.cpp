@@ -52,6 +52,7 @@ hipError_t launch_prefill(void*, const void*, const void*, const void*, const in
                           hipStream_t) {
   return no_device();
 }
+int64_t group_prefix_row_blocks(int max_group_size, int G) { return ((int64_t)max_group_size * G + 95) / 96; }
 hipError_t launch_group_prefix(float*, float*, const void*, const void*, const void*,
                                const int32_t*, const int32_t*, const int32_t*, int, int, int, int,
                                int, int, int, int, int, int, float, hipStream_t) {

@@ -107,9 +107,10 @@ def test_large_group_longer_prefix_partitions(gpu):
 
 
 def test_large_group_eight_heads_head_dim_64(gpu):
-    # 96 sequences (G = 8, D = 64) on a 6144-token prefix: 288 prefix items of four
+    # 96 sequences (G = 8, D = 64) on a 6144-token prefix: 576 prefix items of two
     # sequences at 512 tokens would not fit one per CU, so the group pass runs on the
-    # matrix cores (the 128-row workgroups), then the suffixes, then the reduce
+    # matrix cores (the chunked-prefill kernel's 96-row workgroups), then the suffixes,
+    # then the reduce
     lens = [6144 + 16 + 5 * (i % 7) for i in range(96)]
     b = W.decode_batch(lens, 8, 1, 64, 96 * 3 + 384 + 64, 6204, theta=1e6,
                        shared_prefix=(list(range(96)), 384))
