@@ -304,6 +304,27 @@ def time_each(fn, reps, scrub=None, warm=10):
             "p90_us": round(float(np.percentile(t, 90)), 2), "reps": reps}
 
 
+def issue_mix_table(device, iters=4096, verbose=False):
+    """pa_probe_issue_mix: per launch, each wave runs `iters` iterations of 16 products
+    (mode 1), 32 exp2 + FMA steps per lane (mode 2) or both (mode 3); one to three waves
+    per SIMD (grid = CUs x waves); SIMD cycles per iteration at the nominal 2.4 GHz clock.
+    overlap_saved_frac: the share of the two separate times that running both saves."""
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    table = []
+    for wps in (1, 2, 3):
+        row = {"waves_per_simd": wps}
+        for mode, name in ((1, "products"), (2, "exp2_fma"), (3, "both")):
+            call = probes.prepare_probe_issue_mix(mode, iters, cus * wps, device)
+            us = time_calls(call, 5, warm=2)
+            row[name + "_us"] = round(us, 2)
+            row[name + "_cycles_per_iter"] = round(us * 1e-6 * 2.4e9 / iters)
+        row["overlap_saved_frac"] = round(1 - row["both_us"] / (row["products_us"] + row["exp2_fma_us"]), 3)
+        table.append(row)
+        if verbose:
+            print(json.dumps(row), flush=True)
+    return table
+
+
 def run_ceilings(device, layer_bytes):
     """Measured device limits beside the published ones:
       * a grid-stride streaming read of a 2 GiB buffer (eight times the
@@ -341,7 +362,8 @@ def run_ceilings(device, layer_bytes):
         us = time_calls(probes.prepare_probe_mfma_bf16(iters, grid, device), 3, warm=1)
         best = max(best, grid * 4 * iters * 4 * 16384 / us / 1e6)
     res["mfma_bf16_TFLOPs"] = round(best, 1)
-    res["note"] = ("pa_probe_stream_read, pa_probe_gather_read, pa_probe_mfma_bf16 on this device; "
+    res["issue_mix"] = issue_mix_table(device)
+    res["note"] = ("pa_probe_stream_read, pa_probe_gather_read, pa_probe_mfma_bf16, pa_probe_issue_mix on this device; "
                    "read_ceiling = the faster of the two reads")
     return res
 
@@ -799,24 +821,9 @@ def main():
     torch.cuda.set_device(dev)
 
     if args.mode == "issue-probe":
-        # pa_probe_issue_mix: per launch, each wave runs 4096 iterations of 16 products
-        # (mode 1), 32 exp2 + FMA steps per lane (mode 2) or both (mode 3); one to three
-        # waves per SIMD (grid = CUs x waves); SIMD cycles per iteration at the nominal
-        # 2.4 GHz clock
-        cus = torch.cuda.get_device_properties(dev).multi_processor_count
-        iters = 4096
-        table = []
-        for wps in (1, 2, 3):
-            row = {"waves_per_simd": wps}
-            for mode, name in ((1, "products"), (2, "exp2_fma"), (3, "both")):
-                call = probes.prepare_probe_issue_mix(mode, iters, cus * wps, dev)
-                us = time_calls(call, 5, warm=2)
-                row[name + "_us"] = round(us, 2)
-                row[name + "_cycles_per_iter"] = round(us * 1e-6 * 2.4e9 / iters)
-            row["overlap_saved_frac"] = round(1 - row["both_us"] / (row["products_us"] + row["exp2_fma_us"]), 3)
-            table.append(row)
-            print(json.dumps(row), flush=True)
-        print(json.dumps({"mode": "issue-probe", "iters": iters, "cus": cus, "rows": table}))
+        table = issue_mix_table(dev, verbose=True)
+        print(json.dumps({"mode": "issue-probe", "iters": 4096,
+                          "cus": torch.cuda.get_device_properties(dev).multi_processor_count, "rows": table}))
         return
     if args.mode == "copy-calibration":
         n = 1 << 30
