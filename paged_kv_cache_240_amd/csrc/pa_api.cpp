@@ -84,7 +84,7 @@ int32_t resolve_partition(int32_t partition_size, int32_t B, int32_t Hkv, int32_
 // rows filling two 16-row tiles (NQ * G > 16) move from 512 to 1024 tokens while
 // the 1024-token grid still gives every CU a workgroup.  A 1024-token partition
 // runs as one chunk of 8 waves, two per SIMD, and halves the partials to
-// reduce: measured 29.9 against 33.1 us per call on 16 x 8192 tokens, NQ = 5.
+// reduce: measured 29.4 against 30.9 us per call on 16 x 8192 tokens, NQ = 5.
 int32_t resolve_multi_partition(int32_t partition_size, int32_t B, int32_t NQ, int32_t Hq,
                                 int32_t Hkv, int32_t max_context_len) {
   if (partition_size != -1) return partition_size;
